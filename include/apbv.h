@@ -1,0 +1,162 @@
+/*
+ * apbv.h - C ABI of the APB-V / Spava approximate-attention prefill for MI355X (gfx950).
+ *
+ * The method ("APB-V: Accelerating Long-Video Understanding via Sequence-Parallelism-aware
+ * Approximate Attention", also published as "Spava"; technical summary on gist.science,
+ * section Metodologia) splits the prefill input into an anchor block B_a, context blocks
+ * B^(h) and a query block B_qr. For every context block the hot path
+ *   1. scores the block's keys against the query block and keeps, per KV head, the l_p
+ *      highest-scoring key/value pairs as the block's passing block  (apbv_score_select),
+ *   2. collects the anchor and the passing blocks of all blocks into one prefix per KV head
+ *      (apbv_gather_passing),
+ *   3. runs attention of the block's rows over [anchor | passing blocks of the preceding
+ *      blocks | the block's own keys, causal]                        (apbv_approx_attn_prefill).
+ * All virtual blocks of the method's sequence-parallel layout live on one GPU; ZigZag
+ * pairing of block p with block n-1-p (same page, "Suddivisione del Contesto e
+ * Disposizione ZigZag" and "Bilanciamento del Carico dell'Attenzione Approssimata") is the
+ * work schedule of step 3.
+ *
+ * Conventions shared by every call
+ *  - Tensors are bf16 (raw bit patterns, apbv_bf16) or fp32 / int32, in device memory,
+ *    owned by the caller. The library never allocates, frees or synchronises; every call
+ *    enqueues its kernels on `stream` (a hipStream_t, NULL = the default stream) and
+ *    returns. Kernel faults surface at the caller's next synchronisation.
+ *  - Token-major layouts: q [tokens, hq, d], k/v [tokens, hkv, d]. The row stride (elements
+ *    between consecutive tokens) of q_ctx and of k_ctx/v_ctx may be larger than hq*d /
+ *    hkv*d (for a fused QKV buffer); all other tensors are contiguous.
+ *  - Device pointers and row strides must give 16-byte aligned rows.
+ *  - Query head h uses KV head h / (hq / hkv).
+ *  - `block_starts` is HOST memory: n_blocks + 1 strictly increasing offsets, block_starts[0]
+ *    = 0, block_starts[n_blocks] = N (context tokens; anchor and query block excluded).
+ *  - Every argument is validated before anything is enqueued; on error nothing is launched
+ *    and the call returns a non-zero apbv_status (apbv_last_error() gives details for the
+ *    calling thread). A failed launch returns APBV_EHIP.
+ *  - Calls on one stream may be issued from several threads; the library keeps no mutable
+ *    global state apart from the per-thread error message.
+ */
+#ifndef APBV_H
+#define APBV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t apbv_bf16;   /* raw bf16 bits */
+typedef int32_t apbv_status;
+
+#define APBV_OK 0
+#define APBV_EINVAL 1          /* malformed argument (null pointer, bad sizes, misalignment) */
+#define APBV_EUNSUPPORTED 2    /* well-formed but outside what the kernels implement */
+#define APBV_EWORKSPACE 3      /* workspace missing or too small */
+#define APBV_EHIP 4            /* a HIP launch or query failed */
+
+#define APBV_MAX_BLOCKS 64     /* block_starts travels in kernel arguments */
+
+typedef struct apbv_layout {
+  int32_t n_blocks;            /* virtual context blocks, 1..APBV_MAX_BLOCKS */
+  const int32_t* block_starts; /* HOST [n_blocks + 1] */
+  int32_t l_anchor;            /* anchor rows (>= 0) */
+  int32_t l_query;             /* query-block rows used for scoring (>= 0) */
+  int32_t l_pass;              /* passing rows per block and KV head, 0..min block length */
+  int32_t hq, hkv;             /* query heads and KV heads, hq % hkv == 0 */
+  int32_t head_dim;            /* 64 or 128 */
+  float scale;                 /* softmax scale; 0 means 1/sqrt(head_dim) */
+  int32_t zigzag;              /* 1: ZigZag bucket schedule, 0: block order (same results) */
+  int64_t q_row_stride;        /* elements between tokens of q_ctx; 0 means hq*head_dim */
+  int64_t kv_row_stride;       /* elements between tokens of k_ctx, v_ctx; 0 means hkv*head_dim */
+} apbv_layout;
+
+/* Workspace bytes needed by apbv_score_select for this layout (written to *bytes). */
+apbv_status apbv_score_select_workspace(const apbv_layout* layout, size_t* bytes);
+
+/*
+ * Step 1: passing-block selection (gist.science summary, Metodologia part 1, "Meccanismo di
+ * Attenzione Approssimata", passing blocks chosen by query-to-context attention scores).
+ *
+ * For block v, KV head g and every context row j of block v:
+ *   scores[g, j] = sum over the G = hq/hkv heads h of group g and the l_query query rows i of
+ *                  softmax over the keys j' of block v of (scale * q_query[i,h] . k_ctx[j',g])
+ * (each block's scores sum to G * l_query), computed in fp32 from bf16 inputs with a fixed
+ * reduction order (bitwise reproducible). sel[v, g, :] receives the l_pass rows of block v
+ * with the largest scores, ties to the lower row, as absolute context rows in ascending order.
+ *
+ *   q_query   [l_query, hq, d] bf16, contiguous
+ *   k_ctx     [N, hkv, d] bf16 (kv_row_stride)
+ *   scores    [hkv, N] fp32 out, or NULL (then kept in the workspace)
+ *   sel       [n_blocks, hkv, l_pass] int32 out
+ *   workspace device buffer of at least apbv_score_select_workspace() bytes
+ */
+apbv_status apbv_score_select(const apbv_layout* layout, const apbv_bf16* q_query,
+                              const apbv_bf16* k_ctx, float* scores, int32_t* sel,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Step 2: collect anchor and passing blocks (same page and part: every host gathers the
+ * passing blocks of the hosts before it; on one GPU all of them sit in one prefix buffer).
+ *   k_pre[g] = k_anchor[:, g] ++ k_ctx[sel[0, g], g] ++ ... ++ k_ctx[sel[n-1, g], g]
+ * and the same for v. Block v later reads rows [0, l_anchor + v*l_pass) of its KV head.
+ *
+ *   k_anchor, v_anchor [l_anchor, hkv, d] bf16, contiguous (may be NULL if l_anchor == 0)
+ *   k_ctx, v_ctx       [N, hkv, d] bf16 (kv_row_stride)
+ *   sel                [n_blocks, hkv, l_pass] int32, every entry in [0, N)
+ *   k_pre, v_pre       [hkv, l_anchor + n_blocks*l_pass, d] bf16 out
+ * Out-of-range entries of sel are clamped into [0, N) rather than faulting.
+ */
+apbv_status apbv_gather_passing(const apbv_layout* layout, const apbv_bf16* k_anchor,
+                                const apbv_bf16* v_anchor, const apbv_bf16* k_ctx,
+                                const apbv_bf16* v_ctx, const int32_t* sel, apbv_bf16* k_pre,
+                                apbv_bf16* v_pre, void* stream);
+
+/*
+ * Step 3: approximate attention of the context rows (same page and part: attention over
+ * anchor, passing blocks and local context; "Limitazioni": with one block it is plain
+ * flash attention). Row i of block v, head h, KV head g sees
+ *   k_pre[g, 0 : l_anchor + v*l_pass]  (all visible)  then  k_ctx[block_starts[v] .. i, g]
+ * (causal, diagonal included), softmax in fp32 with scale, bf16 MFMA products:
+ *   out[i, h, :] = softmax(scale * q_ctx[i,h] . keys) @ values        (bf16, round-to-nearest)
+ *   lse[h, i]    = natural-log log-sum-exp of the scaled logits         (fp32, optional)
+ *
+ *   q_ctx        [N, hq, d] bf16 (q_row_stride)
+ *   k_pre, v_pre [hkv, l_anchor + n_blocks*l_pass, d] bf16 (from apbv_gather_passing)
+ *   k_ctx, v_ctx [N, hkv, d] bf16 (kv_row_stride)
+ *   out          [N, hq, d] bf16 out, contiguous
+ *   lse          [hq, N] fp32 out, or NULL
+ *   range_begin, range_end: the part of the work to run. With zigzag = 1 these are ZigZag
+ *     buckets (bucket p = blocks p and n-1-p, apbv_num_buckets() of them), with zigzag = 0
+ *     blocks. (0, 0) runs everything. Rows outside the range are left untouched.
+ * With n_blocks = 1, l_anchor = 0 and l_pass = 0 this is dense causal attention.
+ */
+apbv_status apbv_approx_attn_prefill(const apbv_layout* layout, const apbv_bf16* q_ctx,
+                                     const apbv_bf16* k_pre, const apbv_bf16* v_pre,
+                                     const apbv_bf16* k_ctx, const apbv_bf16* v_ctx,
+                                     apbv_bf16* out, float* lse, int32_t range_begin,
+                                     int32_t range_end, void* stream);
+
+/* Number of schedulable ranges: ZigZag buckets (ceil(n/2)) if zigzag, else n_blocks.
+ * Returns -1 for an invalid layout. Host only. */
+int32_t apbv_num_buckets(const apbv_layout* layout);
+
+/* Host-only view of the attention work list for [range_begin, range_end): *count receives
+ * the number of work units; if `units` is non-NULL and capacity >= *count, unit u is
+ * written as 4 ints {block_a, tile_a, block_b, tile_b} (-1 when a unit has one part).
+ * Tile t of block v is context rows [bs[v] + t*rows, min(bs[v] + (t+1)*rows, bs[v+1])) with
+ * rows = apbv_attn_tile_rows(head_dim). Every unit is launched for all hq heads. */
+apbv_status apbv_schedule(const apbv_layout* layout, int32_t range_begin, int32_t range_end,
+                          int32_t* units, int32_t capacity, int32_t* count);
+
+/* Query rows per attention work tile for a head dimension (0 if unsupported). */
+int32_t apbv_attn_tile_rows(int32_t head_dim);
+
+const char* apbv_status_str(apbv_status status);
+/* Detail of the calling thread's most recent failed call ("" if none). */
+const char* apbv_last_error(void);
+/* Library version string. */
+const char* apbv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* APBV_H */

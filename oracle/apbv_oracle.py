@@ -58,22 +58,25 @@ def kv_head(h: int, hq: int, hkv: int) -> int:
 # --------------------------------------------------------------------------------------
 # Step 1 - query-to-context scores of every block (the passing-block criterion).
 # --------------------------------------------------------------------------------------
-def passing_scores(q_query, k_ctx, block_starts, hq: int, hkv: int, scale: float) -> np.ndarray:
+def passing_scores(q_query, k_ctx, block_starts, hq: int, hkv: int, scale: float,
+                   blocks=None) -> np.ndarray:
     """Scores s[g, j] of every context key, float64 ``[hkv, N]``.
 
     For block v (rows bs[v]..bs[v+1]) and KV head g, every query-block row i of every head h
     in g's group spreads a softmax over block v's keys; s is the sum of those distributions
     (heads ascending, then rows ascending). Each block's scores sum to G * l_q.
+    ``blocks`` restricts the work to some blocks (the others are left as NaN).
     """
     q = _as64(q_query)             # [l_q, hq, d]
-    k = _as64(k_ctx)               # [N, hkv, d]
     bs = np.asarray(block_starts, np.int64)
-    s = np.zeros((hkv, k.shape[0]), np.float64)
-    for v in range(bs.size - 1):
+    s = np.full((hkv, np.asarray(k_ctx).shape[0]), np.nan)
+    for v in (range(bs.size - 1) if blocks is None else blocks):
         lo, hi = int(bs[v]), int(bs[v + 1])
+        k = _as64(k_ctx[lo:hi])    # [L_v, hkv, d]
+        s[:, lo:hi] = 0.0
         for h in range(hq):
             g = kv_head(h, hq, hkv)
-            z = scale * (q[:, h, :] @ k[lo:hi, g, :].T)          # [l_q, L_v]
+            z = scale * (q[:, h, :] @ k[:, g, :].T)             # [l_q, L_v]
             s[g, lo:hi] += _softmax_rows(z).sum(axis=0)
     return s
 
@@ -106,13 +109,14 @@ def select_passing(scores32, block_starts, l_pass: int) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 def gather_prefix(k_anchor, v_anchor, k_ctx, v_ctx, sel):
     """``K_pre, V_pre`` float64 ``[hkv, l_a + n * l_pass, d]``: anchor, then passing 0..n-1."""
-    ka, va, kc, vc = (_as64(x) for x in (k_anchor, v_anchor, k_ctx, v_ctx))
+    ka, va = _as64(k_anchor), _as64(v_anchor)
+    kc, vc = np.asarray(k_ctx), np.asarray(v_ctx)   # rows are widened once gathered
     sel = np.asarray(sel, np.int64)
     n, hkv, _ = sel.shape
     k_pre, v_pre = [], []
     for g in range(hkv):
-        k_parts = [ka[:, g, :]] + [kc[sel[v, g], g, :] for v in range(n)]
-        v_parts = [va[:, g, :]] + [vc[sel[v, g], g, :] for v in range(n)]
+        k_parts = [ka[:, g, :]] + [_as64(kc[sel[v, g], g, :]) for v in range(n)]
+        v_parts = [va[:, g, :]] + [_as64(vc[sel[v, g], g, :]) for v in range(n)]
         k_pre.append(np.concatenate(k_parts, axis=0))
         v_pre.append(np.concatenate(v_parts, axis=0))
     return np.stack(k_pre), np.stack(v_pre)
@@ -130,9 +134,9 @@ def attend(q_ctx, k_pre, v_pre, k_ctx, v_ctx, block_starts, l_anchor: int, l_pas
     log-sum-exp of the scaled logits. ``rows`` (sorted absolute rows) and ``heads`` restrict
     the work to a sample; entries outside the sample are left as NaN.
     """
-    q, kp, vp, kc, vc = (_as64(x) for x in (q_ctx, k_pre, v_pre, k_ctx, v_ctx))
+    kp, vp = _as64(k_pre), _as64(v_pre)
     bs = np.asarray(block_starts, np.int64)
-    N, d = q.shape[0], q.shape[2]
+    N, d = np.asarray(q_ctx).shape[0], np.asarray(q_ctx).shape[2]
     out = np.full((N, hq, d), np.nan)
     lse = np.full((hq, N), np.nan)
     all_rows = np.arange(N) if rows is None else np.asarray(rows, np.int64)
@@ -143,14 +147,15 @@ def attend(q_ctx, k_pre, v_pre, k_ctx, v_ctx, block_starts, l_anchor: int, l_pas
         if mine.size == 0:
             continue
         P = l_anchor + v * l_pass
+        kc, vc = _as64(k_ctx[lo:hi]), _as64(v_ctx[lo:hi])
         for h in heads:
             g = kv_head(h, hq, hkv)
-            keys = np.concatenate([kp[g, :P], kc[lo:hi, g]], axis=0)
-            vals = np.concatenate([vp[g, :P], vc[lo:hi, g]], axis=0)
+            keys = np.concatenate([kp[g, :P], kc[:, g]], axis=0)
+            vals = np.concatenate([vp[g, :P], vc[:, g]], axis=0)
             local_pos = np.arange(hi - lo)
             for c in range(0, mine.size, row_chunk):
                 r = mine[c:c + row_chunk]
-                z = scale * (q[r, h, :] @ keys.T)                     # [rows, P + L_v]
+                z = scale * (_as64(q_ctx[r, h, :]) @ keys.T)          # [rows, P + L_v]
                 z[:, P:][local_pos[None, :] > (r - lo)[:, None]] = -np.inf
                 m = np.max(z, axis=1, keepdims=True)
                 e = np.exp(z - m)

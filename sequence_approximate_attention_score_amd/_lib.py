@@ -1,0 +1,188 @@
+"""ctypes binding of ``libapbv.so`` (argument marshalling only).
+
+Every step of the hot path runs in the library's HIP kernels; this module converts torch
+tensors into device pointers, allocates outputs the caller did not provide (torch is the
+device-memory and stream plumbing) and raises ``ApbvError`` on a non-zero status.
+Importing it fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libapbv.so")
+
+APBV_OK, APBV_EINVAL, APBV_EUNSUPPORTED, APBV_EWORKSPACE, APBV_EHIP = 0, 1, 2, 3, 4
+MAX_BLOCKS = 64
+
+EXPORTED = ["apbv_score_select_workspace", "apbv_score_select", "apbv_gather_passing",
+            "apbv_approx_attn_prefill", "apbv_num_buckets", "apbv_schedule",
+            "apbv_attn_tile_rows", "apbv_status_str", "apbv_last_error", "apbv_version"]
+
+
+class ApbvError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("n_blocks", ctypes.c_int32), ("block_starts", ctypes.POINTER(ctypes.c_int32)),
+                ("l_anchor", ctypes.c_int32), ("l_query", ctypes.c_int32), ("l_pass", ctypes.c_int32),
+                ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("zigzag", ctypes.c_int32),
+                ("q_row_stride", ctypes.c_int64), ("kv_row_stride", ctypes.c_int64)]
+
+
+_VP, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+_LP = ctypes.POINTER(_Layout)
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m sequence_approximate_attention_score_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "apbv_score_select_workspace": (_I32, [_LP, ctypes.POINTER(_SZ)]),
+            "apbv_score_select": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+            "apbv_gather_passing": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+            "apbv_approx_attn_prefill": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
+            "apbv_num_buckets": (_I32, [_LP]),
+            "apbv_schedule": (_I32, [_LP, _I32, _I32, _VP, _I32, ctypes.POINTER(_I32)]),
+            "apbv_attn_tile_rows": (_I32, [_I32]),
+            "apbv_status_str": (ctypes.c_char_p, [_I32]),
+            "apbv_last_error": (ctypes.c_char_p, []),
+            "apbv_version": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != APBV_OK:
+        L = lib()
+        raise ApbvError(status, where, f"{L.apbv_status_str(status).decode()}: "
+                                       f"{L.apbv_last_error().decode()}")
+
+
+class Layout:
+    """Host-side layout of one problem (mirrors ``apbv_layout``)."""
+
+    def __init__(self, block_starts, *, l_anchor: int, l_query: int, l_pass: int, hq: int,
+                 hkv: int, head_dim: int, scale: float = 0.0, zigzag: bool = True,
+                 q_row_stride: int = 0, kv_row_stride: int = 0):
+        bs = np.ascontiguousarray(np.asarray(block_starts, dtype=np.int32))
+        self._bs = bs
+        self.block_starts = bs
+        self.n_blocks = int(bs.size - 1)
+        self.l_anchor, self.l_query, self.l_pass = int(l_anchor), int(l_query), int(l_pass)
+        self.hq, self.hkv, self.head_dim = int(hq), int(hkv), int(head_dim)
+        self.n_tokens = int(bs[-1]) if bs.size else 0
+        self.pre_rows = self.l_anchor + self.n_blocks * self.l_pass
+        self.c = _Layout(self.n_blocks, bs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                         self.l_anchor, self.l_query, self.l_pass, self.hq, self.hkv,
+                         self.head_dim, float(scale), int(bool(zigzag)), int(q_row_stride),
+                         int(kv_row_stride))
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def num_buckets(layout: Layout) -> int:
+    n = lib().apbv_num_buckets(layout.ref())
+    if n < 0:
+        _check(APBV_EINVAL, "apbv_num_buckets")
+    return n
+
+
+def attn_tile_rows(head_dim: int) -> int:
+    return lib().apbv_attn_tile_rows(head_dim)
+
+
+def schedule(layout: Layout, range_begin: int = 0, range_end: int = 0) -> np.ndarray:
+    """Work units of the attention launch as an int32 array [units, 4] (host only)."""
+    L = lib()
+    cnt = _I32(0)
+    _check(L.apbv_schedule(layout.ref(), range_begin, range_end, None, 0, ctypes.byref(cnt)),
+           "apbv_schedule")
+    out = np.zeros((cnt.value, 4), np.int32)
+    _check(L.apbv_schedule(layout.ref(), range_begin, range_end, out.ctypes.data_as(_VP),
+                           cnt.value, ctypes.byref(cnt)), "apbv_schedule")
+    return out
+
+
+def score_select_workspace(layout: Layout) -> int:
+    n = _SZ(0)
+    _check(lib().apbv_score_select_workspace(layout.ref(), ctypes.byref(n)),
+           "apbv_score_select_workspace")
+    return n.value
+
+
+def score_select(layout: Layout, q_query, k_ctx, *, scores=None, sel=None, workspace=None,
+                 want_scores: bool = True):
+    """Step 1 (scores + top-l_p). Returns (scores or None, sel)."""
+    import torch
+    dev = k_ctx.device
+    if want_scores and scores is None:
+        scores = torch.empty((layout.hkv, layout.n_tokens), dtype=torch.float32, device=dev)
+    if sel is None:
+        sel = torch.empty((layout.n_blocks, layout.hkv, layout.l_pass), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(score_select_workspace(layout), 256), dtype=torch.uint8, device=dev)
+    _check(lib().apbv_score_select(layout.ref(), _ptr(q_query), _ptr(k_ctx), _ptr(scores),
+                                   _ptr(sel), _ptr(workspace), workspace.numel(), _stream(dev)),
+           "apbv_score_select")
+    return scores, sel
+
+
+def gather_passing(layout: Layout, k_anchor, v_anchor, k_ctx, v_ctx, sel, *, k_pre=None,
+                   v_pre=None):
+    """Step 2 (anchor + passing prefix per KV head). Returns (k_pre, v_pre)."""
+    import torch
+    shape = (layout.hkv, layout.pre_rows, layout.head_dim)
+    if k_pre is None:
+        k_pre = torch.empty(shape, dtype=torch.bfloat16, device=k_ctx.device)
+    if v_pre is None:
+        v_pre = torch.empty(shape, dtype=torch.bfloat16, device=k_ctx.device)
+    _check(lib().apbv_gather_passing(layout.ref(), _ptr(k_anchor), _ptr(v_anchor), _ptr(k_ctx),
+                                     _ptr(v_ctx), _ptr(sel), _ptr(k_pre), _ptr(v_pre),
+                                     _stream(k_ctx.device)), "apbv_gather_passing")
+    return k_pre, v_pre
+
+
+def approx_attn_prefill(layout: Layout, q_ctx, k_pre, v_pre, k_ctx, v_ctx, *, out=None, lse=None,
+                        want_lse: bool = False, range_begin: int = 0, range_end: int = 0):
+    """Step 3 (attention over [anchor | passing | causal local]). Returns (out, lse or None)."""
+    import torch
+    if out is None:
+        out = torch.empty((layout.n_tokens, layout.hq, layout.head_dim), dtype=torch.bfloat16,
+                          device=q_ctx.device)
+    if want_lse and lse is None:
+        lse = torch.empty((layout.hq, layout.n_tokens), dtype=torch.float32, device=q_ctx.device)
+    _check(lib().apbv_approx_attn_prefill(layout.ref(), _ptr(q_ctx), _ptr(k_pre), _ptr(v_pre),
+                                          _ptr(k_ctx), _ptr(v_ctx), _ptr(out), _ptr(lse),
+                                          range_begin, range_end, _stream(q_ctx.device)),
+           "apbv_approx_attn_prefill")
+    return out, lse
+
+
+def version() -> str:
+    return lib().apbv_version().decode()

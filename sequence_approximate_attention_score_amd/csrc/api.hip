@@ -1,0 +1,312 @@
+// C ABI of the approximate-attention prefill: argument validation, work schedule and
+// launches. All checks run on the host before anything is enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "apbv_internal.h"
+
+namespace apbv {
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+apbv_status fail(apbv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Checked {
+  int n, N, hq, hkv, d, G, l_a, l_q, l_p, pre_rows, min_block, max_block;
+  int64_t q_stride, kv_stride;
+  float scale;
+};
+
+apbv_status check_layout(const apbv_layout* L, Checked& c) {
+  if (L == nullptr) return fail(APBV_EINVAL, "layout is NULL");
+  if (L->n_blocks < 1 || L->n_blocks > APBV_MAX_BLOCKS)
+    return fail(APBV_EINVAL, "n_blocks = %d outside 1..%d", L->n_blocks, APBV_MAX_BLOCKS);
+  if (L->block_starts == nullptr) return fail(APBV_EINVAL, "block_starts is NULL");
+  if (L->block_starts[0] != 0) return fail(APBV_EINVAL, "block_starts[0] = %d, expected 0", L->block_starts[0]);
+  c.min_block = 0x7fffffff;
+  c.max_block = 0;
+  for (int v = 0; v < L->n_blocks; ++v) {
+    const int64_t len = (int64_t)L->block_starts[v + 1] - L->block_starts[v];
+    if (len <= 0) return fail(APBV_EINVAL, "block_starts not strictly increasing at block %d", v);
+    c.min_block = len < c.min_block ? (int)len : c.min_block;
+    c.max_block = len > c.max_block ? (int)len : c.max_block;
+  }
+  c.n = L->n_blocks;
+  c.N = L->block_starts[c.n];
+  if (L->hq <= 0 || L->hkv <= 0 || L->hq % L->hkv != 0)
+    return fail(APBV_EINVAL, "hq = %d, hkv = %d: need positive with hq %% hkv == 0", L->hq, L->hkv);
+  if (L->head_dim != 64 && L->head_dim != 128)
+    return fail(APBV_EUNSUPPORTED, "head_dim = %d (supported: 64, 128)", L->head_dim);
+  if (L->l_anchor < 0 || L->l_query < 0 || L->l_pass < 0)
+    return fail(APBV_EINVAL, "negative l_anchor / l_query / l_pass");
+  if (L->l_pass > c.min_block)
+    return fail(APBV_EINVAL, "l_pass = %d exceeds the shortest block (%d)", L->l_pass, c.min_block);
+  if (L->zigzag != 0 && L->zigzag != 1) return fail(APBV_EINVAL, "zigzag must be 0 or 1");
+  if (!(L->scale >= 0.f) || isinf(L->scale)) return fail(APBV_EINVAL, "scale must be finite and >= 0");
+  c.hq = L->hq;
+  c.hkv = L->hkv;
+  c.d = L->head_dim;
+  c.G = L->hq / L->hkv;
+  c.l_a = L->l_anchor;
+  c.l_q = L->l_query;
+  c.l_p = L->l_pass;
+  const int64_t pre = (int64_t)c.l_a + (int64_t)c.n * c.l_p;
+  if (pre > 0x7fffffff) return fail(APBV_EUNSUPPORTED, "prefix rows overflow int32");
+  c.pre_rows = (int)pre;
+  c.scale = L->scale == 0.f ? 1.0f / sqrtf((float)c.d) : L->scale;
+  c.q_stride = L->q_row_stride == 0 ? (int64_t)c.hq * c.d : L->q_row_stride;
+  c.kv_stride = L->kv_row_stride == 0 ? (int64_t)c.hkv * c.d : L->kv_row_stride;
+  if (c.q_stride < (int64_t)c.hq * c.d || c.q_stride % 8 != 0)
+    return fail(APBV_EINVAL, "q_row_stride = %lld must be >= hq*head_dim and a multiple of 8",
+                (long long)c.q_stride);
+  if (c.kv_stride < (int64_t)c.hkv * c.d || c.kv_stride % 8 != 0)
+    return fail(APBV_EINVAL, "kv_row_stride = %lld must be >= hkv*head_dim and a multiple of 8",
+                (long long)c.kv_stride);
+  if ((int64_t)c.G * c.l_q > 0x7fffffff / 2) return fail(APBV_EUNSUPPORTED, "too many score rows");
+  return APBV_OK;
+}
+
+apbv_status check_ptr(const void* p, const char* name, bool needed) {
+  if (!needed) return APBV_OK;
+  if (p == nullptr) return fail(APBV_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(APBV_EINVAL, "%s is not 16-byte aligned", name);
+  return APBV_OK;
+}
+
+#define APBV_TRY(expr)                   \
+  do {                                   \
+    const apbv_status _s = (expr);       \
+    if (_s != APBV_OK) return _s;        \
+  } while (0)
+
+int n_split_of(const Checked& c) { return (c.max_block + kScoreSplit - 1) / kScoreSplit; }
+
+}  // namespace
+
+void build_schedule(Schedule& s, int32_t n_blocks, const int32_t* bs, int32_t zigzag,
+                    int32_t tile_rows) {
+  memset(&s, 0, sizeof(s));
+  s.n_blocks = n_blocks;
+  s.zigzag = zigzag;
+  s.tile_rows = tile_rows;
+  for (int v = 0; v <= n_blocks; ++v) s.bs[v] = bs[v];
+  s.tiles_before[0] = 0;
+  for (int v = 0; v < n_blocks; ++v) s.tiles_before[v + 1] = s.tiles_before[v] + s.tiles(v);
+  const int nb = (n_blocks + 1) / 2;
+  s.bucket_units[0] = 0;
+  for (int b = 0; b < nb; ++b) {
+    const int a = b, c = n_blocks - 1 - b;
+    const int units = a != c ? (s.tiles(a) > s.tiles(c) ? s.tiles(a) : s.tiles(c))
+                             : (s.tiles(a) + 1) / 2;
+    s.bucket_units[b + 1] = s.bucket_units[b] + units;
+  }
+}
+
+}  // namespace apbv
+
+using namespace apbv;
+
+extern "C" {
+
+const char* apbv_version(void) { return "apbv-gfx950 0.1.0"; }
+
+const char* apbv_last_error(void) { return g_err; }
+
+const char* apbv_status_str(apbv_status s) {
+  switch (s) {
+    case APBV_OK: return "ok";
+    case APBV_EINVAL: return "invalid argument";
+    case APBV_EUNSUPPORTED: return "unsupported configuration";
+    case APBV_EWORKSPACE: return "workspace missing or too small";
+    case APBV_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int32_t apbv_attn_tile_rows(int32_t head_dim) { return attn_tile_rows(head_dim); }
+
+int32_t apbv_num_buckets(const apbv_layout* layout) {
+  Checked c;
+  if (check_layout(layout, c) != APBV_OK) return -1;
+  return layout->zigzag ? (c.n + 1) / 2 : c.n;
+}
+
+apbv_status apbv_score_select_workspace(const apbv_layout* layout, size_t* bytes) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  if (bytes == nullptr) return fail(APBV_EINVAL, "bytes is NULL");
+  *bytes = score_workspace_bytes(c.n, c.hkv, c.G * c.l_q, n_split_of(c), c.N, true);
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_score_select(const apbv_layout* layout, const apbv_bf16* q_query,
+                              const apbv_bf16* k_ctx, float* scores, int32_t* sel,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  APBV_TRY(check_ptr(q_query, "q_query", c.l_q > 0));
+  APBV_TRY(check_ptr(k_ctx, "k_ctx", true));
+  APBV_TRY(check_ptr(sel, "sel", c.l_p > 0));
+  if (scores != nullptr && ((uintptr_t)scores & 3u) != 0)
+    return fail(APBV_EINVAL, "scores is not 4-byte aligned");
+  const int rows = c.G * c.l_q;
+  const int n_split = n_split_of(c);
+  const size_t need = score_workspace_bytes(c.n, c.hkv, rows, n_split, c.N, scores == nullptr);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(APBV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (workspace != nullptr && ((uintptr_t)workspace & 255u) != 0)
+    return fail(APBV_EINVAL, "workspace is not 256-byte aligned");
+
+  ScoreParams p;
+  memset(&p, 0, sizeof(p));
+  p.qq = q_query;
+  p.kc = k_ctx;
+  p.stats = reinterpret_cast<float2*>(workspace);
+  const size_t stats_bytes = (((size_t)c.n * c.hkv * n_split * rows * sizeof(float2)) + 255) & ~(size_t)255;
+  p.scores = scores != nullptr ? scores
+                               : reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes);
+  p.sel = sel;
+  p.kv_stride = c.kv_stride;
+  p.hq = c.hq;
+  p.hkv = c.hkv;
+  p.group = c.G;
+  p.l_query = c.l_q;
+  p.rows = rows;
+  p.n_tokens = c.N;
+  p.n_blocks = c.n;
+  p.n_split = n_split;
+  p.l_pass = c.l_p;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+  for (int v = 0; v <= c.n; ++v) p.bs[v] = layout->block_starts[v];
+  const hipError_t e = launch_score_select(p, c.d, c.max_block, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(APBV_EHIP, "score/select launch: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_gather_passing(const apbv_layout* layout, const apbv_bf16* k_anchor,
+                                const apbv_bf16* v_anchor, const apbv_bf16* k_ctx,
+                                const apbv_bf16* v_ctx, const int32_t* sel, apbv_bf16* k_pre,
+                                apbv_bf16* v_pre, void* stream) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  APBV_TRY(check_ptr(k_anchor, "k_anchor", c.l_a > 0));
+  APBV_TRY(check_ptr(v_anchor, "v_anchor", c.l_a > 0));
+  APBV_TRY(check_ptr(k_ctx, "k_ctx", c.l_p > 0));
+  APBV_TRY(check_ptr(v_ctx, "v_ctx", c.l_p > 0));
+  APBV_TRY(check_ptr(sel, "sel", c.l_p > 0));
+  APBV_TRY(check_ptr(k_pre, "k_pre", c.pre_rows > 0));
+  APBV_TRY(check_ptr(v_pre, "v_pre", c.pre_rows > 0));
+  GatherParams p;
+  memset(&p, 0, sizeof(p));
+  p.ka = k_anchor;
+  p.va = v_anchor;
+  p.kc = k_ctx;
+  p.vc = v_ctx;
+  p.sel = sel;
+  p.kpre = k_pre;
+  p.vpre = v_pre;
+  p.kv_stride = c.kv_stride;
+  p.hkv = c.hkv;
+  p.l_anchor = c.l_a;
+  p.l_pass = c.l_p;
+  p.n_blocks = c.n;
+  p.pre_rows = c.pre_rows;
+  p.n_tokens = c.N;
+  const hipError_t e = launch_gather(p, c.d, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(APBV_EHIP, "gather launch: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_schedule(const apbv_layout* layout, int32_t range_begin, int32_t range_end,
+                          int32_t* units, int32_t capacity, int32_t* count) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  if (count == nullptr) return fail(APBV_EINVAL, "count is NULL");
+  Schedule s;
+  build_schedule(s, c.n, layout->block_starts, layout->zigzag, attn_tile_rows(c.d));
+  const int nb = s.n_buckets();
+  if (range_begin == 0 && range_end == 0) range_end = nb;
+  if (range_begin < 0 || range_end > nb || range_begin > range_end)
+    return fail(APBV_EINVAL, "range [%d, %d) outside [0, %d]", range_begin, range_end, nb);
+  const int u0 = s.units_before(range_begin), u1 = s.units_before(range_end);
+  *count = u1 - u0;
+  if (units != nullptr) {
+    if (capacity < *count) return fail(APBV_EINVAL, "capacity %d < %d units", capacity, *count);
+    for (int u = u0; u < u1; ++u) {
+      int va, ta, vb, tb;
+      s.decode(u, va, ta, vb, tb);
+      int32_t* o = units + 4 * (u - u0);
+      o[0] = va; o[1] = va >= 0 ? ta : -1; o[2] = vb; o[3] = vb >= 0 ? tb : -1;
+    }
+  }
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_approx_attn_prefill(const apbv_layout* layout, const apbv_bf16* q_ctx,
+                                     const apbv_bf16* k_pre, const apbv_bf16* v_pre,
+                                     const apbv_bf16* k_ctx, const apbv_bf16* v_ctx,
+                                     apbv_bf16* out, float* lse, int32_t range_begin,
+                                     int32_t range_end, void* stream) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  APBV_TRY(check_ptr(q_ctx, "q_ctx", true));
+  APBV_TRY(check_ptr(k_ctx, "k_ctx", true));
+  APBV_TRY(check_ptr(v_ctx, "v_ctx", true));
+  APBV_TRY(check_ptr(k_pre, "k_pre", c.pre_rows > 0));
+  APBV_TRY(check_ptr(v_pre, "v_pre", c.pre_rows > 0));
+  APBV_TRY(check_ptr(out, "out", true));
+  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return fail(APBV_EINVAL, "lse is not 4-byte aligned");
+  if ((int64_t)c.hq * c.N > 0x7fffffffLL * 8) return fail(APBV_EUNSUPPORTED, "problem too large");
+
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  build_schedule(p.sched, c.n, layout->block_starts, layout->zigzag, attn_tile_rows(c.d));
+  const int nb = p.sched.n_buckets();
+  if (range_begin == 0 && range_end == 0) range_end = nb;
+  if (range_begin < 0 || range_end > nb || range_begin > range_end)
+    return fail(APBV_EINVAL, "range [%d, %d) outside [0, %d]", range_begin, range_end, nb);
+  p.q = q_ctx;
+  p.kpre = k_pre;
+  p.vpre = v_pre;
+  p.kc = k_ctx;
+  p.vc = v_ctx;
+  p.out = out;
+  p.lse = lse;
+  p.q_stride = c.q_stride;
+  p.kv_stride = c.kv_stride;
+  p.hq = c.hq;
+  p.hkv = c.hkv;
+  p.group = c.G;
+  p.l_anchor = c.l_a;
+  p.l_pass = c.l_p;
+  p.pre_rows = c.pre_rows;
+  p.n_tokens = c.N;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+  p.unit_begin = p.sched.units_before(range_begin);
+  p.n_units = p.sched.units_before(range_end) - p.unit_begin;
+  if ((uint64_t)p.n_units * (uint64_t)p.hq >= (1ull << 32))
+    return fail(APBV_EUNSUPPORTED, "grid too large");
+  const hipError_t e = launch_attention(p, c.d, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(APBV_EHIP, "attention launch: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,327 @@
+// Passing-block selection for gfx950: query-to-context scores and per-(block, KV head)
+// top-l_p (APB-V technical summary on gist.science, Metodologia part 1, "Meccanismo di
+// Attenzione Approssimata": every host keeps the key/value pairs that its query-to-context
+// attention scores rank highest, and hands them on as its passing block).
+//
+// Score of key j of block v, KV head g (R = G * l_query score rows, row r = head g*G + r/l_q,
+// query row r % l_q):
+//     s[g, j] = sum_r softmax_{j' in block v}(scale * q_r . k_j')_j
+// Three kernels, all with a fixed reduction order (results are bitwise reproducible):
+//   1. row statistics: per (block, KV head, 128-row group, 2048-key split) the running max
+//      (log2 units) and sum of exp2 of each row; S^T = K . Q^T on MFMA puts one row per lane.
+//   2. column sums: per (block, KV head, 256-key tile) the split statistics are folded into
+//      each row's log-sum-exp, S = Q . K^T is recomputed on MFMA (one key per lane) and the
+//      probabilities are summed down the rows.
+//   3. selection: per (block, KV head) an exact radix select of the l_p-th largest score on
+//      order-preserving 32-bit keys, then a stable compaction (ties to the lower row) that
+//      writes the chosen rows in ascending order.
+#include "apbv_device.h"
+#include "apbv_internal.h"
+
+namespace apbv {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKeyTile = 64;        // keys per LDS tile in the row-statistics kernel
+constexpr int kColKeys = 256;       // keys per column-sum workgroup (64 per wave)
+constexpr int kQChunk = 128;        // query rows staged in LDS at a time (column sums)
+
+// ------------------------------------------------------------------ 1. row statistics
+template <int D>
+__global__ __launch_bounds__(kThreads) void score_rowstats(const ScoreParams p) {
+  constexpr int NK = D / 16;
+  constexpr int KSTR = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kKeyTile * KSTR];
+
+  const int n_rg = (p.rows + 127) / 128;
+  int b = blockIdx.x;
+  const int split = b % p.n_split; b /= p.n_split;
+  const int rg = b % n_rg; b /= n_rg;
+  const int g = b % p.hkv;
+  const int v = b / p.hkv;
+  const int lo = p.bs[v], hi = p.bs[v + 1];
+  const int k_begin = lo + split * kScoreSplit;
+  if (k_begin >= hi) return;   // the combiner reads only splits that hold keys
+  const int k_end = min(hi, k_begin + kScoreSplit);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int row = rg * 128 + wave * 32 + l32;
+  bf16x8 qf[NK];
+  {
+    const bool ok = row < p.rows;
+    const int h = g * p.group + (ok ? row / p.l_query : 0);
+    const int qi = ok ? row % p.l_query : 0;
+    const uint16_t* qrow = p.qq + ((int64_t)qi * p.hq + h) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      qf[ks] = as_bf16x8(ok ? load16(qrow + ks * 16) : u32x4{0, 0, 0, 0});
+  }
+
+  float m = -INFINITY, l = 0.f;   // raw-logit max, sum of exp2((s - m) * c) over this lane's keys
+  for (int k0 = k_begin; k0 < k_end; k0 += kKeyTile) {
+    const int valid = min(kKeyTile, k_end - k0);
+    __syncthreads();
+    for (int c = threadIdx.x; c < kKeyTile * D / 8; c += kThreads) {
+      const int kr = c / (D / 8), col = c % (D / 8);
+      const u32x4 val = kr < valid ? load16(p.kc + (int64_t)(k0 + kr) * p.kv_stride + g * D + col * 8)
+                                   : u32x4{0, 0, 0, 0};
+      store16(sK + kr * KSTR + col * 8, val);
+    }
+    __syncthreads();
+    f32x16 s[kKeyTile / 32];
+#pragma unroll
+    for (int n = 0; n < kKeyTile / 32; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[n][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+      for (int n = 0; n < kKeyTile / 32; ++n) {
+        const bf16x8 a = as_bf16x8(load16(sK + (n * 32 + l32) * KSTR + ks * 16 + half * 8));
+        s[n] = mfma32(a, qf[ks], s[n]);
+      }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < kKeyTile / 32; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = n * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        if (kk >= valid) s[n][r] = -INFINITY;
+        mx = fmaxf(mx, s[n][r]);
+      }
+    mx = fmaxf(mx, swap_half(mx));
+    const float mn = fmaxf(m, mx);
+    float acc = l * fast_exp2((m - mn) * p.scale_log2);
+    if (m == -INFINITY) acc = 0.f;
+#pragma unroll
+    for (int n = 0; n < kKeyTile / 32; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc += fast_exp2((s[n][r] - mn) * p.scale_log2);
+    m = mn;
+    l = acc;
+  }
+  l += swap_half(l);
+  if (half == 0 && row < p.rows) {
+    const int64_t idx = (((int64_t)v * p.hkv + g) * p.n_split + split) * p.rows + row;
+    p.stats[idx] = make_float2(m * p.scale_log2, l);
+  }
+}
+
+// ------------------------------------------------------------------ 2. column sums
+template <int D>
+__global__ __launch_bounds__(kThreads) void score_colsum(const ScoreParams p, int rows_pad) {
+  constexpr int NK = D / 16;
+  constexpr int QSTR = D + 8;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem);                   // [kQChunk][QSTR]
+  float* sL = reinterpret_cast<float*>(smem + kQChunk * QSTR * 2);     // [rows_pad] lse2
+
+  const int n_kt = (gridDim.x / (p.n_blocks * p.hkv));
+  int b = blockIdx.x;
+  const int kt = b % n_kt; b /= n_kt;
+  const int g = b % p.hkv;
+  const int v = b / p.hkv;
+  const int lo = p.bs[v], hi = p.bs[v + 1];
+  const int kbase = lo + kt * kColKeys;
+  if (kbase >= hi) return;
+
+  // row log-sum-exp (log2 units) from the split statistics, splits in order
+  const int nsp = (hi - lo + kScoreSplit - 1) / kScoreSplit;
+  const float2* st = p.stats + ((int64_t)v * p.hkv + g) * p.n_split * p.rows;
+  for (int r = threadIdx.x; r < rows_pad; r += kThreads) {
+    float out = INFINITY;   // padding rows contribute exp2(-inf) = 0
+    if (r < p.rows) {
+      float M = -INFINITY;
+      for (int s = 0; s < nsp; ++s) M = fmaxf(M, st[(int64_t)s * p.rows + r].x);
+      float L = 0.f;
+      for (int s = 0; s < nsp; ++s) {
+        const float2 ml = st[(int64_t)s * p.rows + r];
+        L += ml.y * fast_exp2(ml.x - M);
+      }
+      out = M + fast_log2(L);
+    }
+    sL[r] = out;
+  }
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  // K^T fragments (B operand): lane holds key l32 of each of the wave's two 32-key groups
+  bf16x8 kf[2][NK];
+  int key[2];
+#pragma unroll
+  for (int kg = 0; kg < 2; ++kg) {
+    key[kg] = kbase + wave * 64 + kg * 32 + l32;
+    const bool ok = key[kg] < hi;
+    const uint16_t* krow = p.kc + (int64_t)(ok ? key[kg] : lo) * p.kv_stride + g * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      kf[kg][ks] = as_bf16x8(ok ? load16(krow + ks * 16) : u32x4{0, 0, 0, 0});
+  }
+
+  float col[2] = {0.f, 0.f};
+  for (int c0 = 0; c0 < p.rows; c0 += kQChunk) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < kQChunk * D / 8; c += kThreads) {
+      const int qr = c / (D / 8), cc = c % (D / 8);
+      const int r = c0 + qr;
+      u32x4 val = {0, 0, 0, 0};
+      if (r < p.rows) {
+        const int h = g * p.group + r / p.l_query, qi = r % p.l_query;
+        val = load16(p.qq + ((int64_t)qi * p.hq + h) * D + cc * 8);
+      }
+      store16(sQ + qr * QSTR + cc * 8, val);
+    }
+    __syncthreads();
+    const int nrb = min(kQChunk, p.rows - c0 + 31) / 32;
+    for (int rb = 0; rb < nrb; ++rb) {
+      bf16x8 af[NK];
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks)
+        af[ks] = as_bf16x8(load16(sQ + (rb * 32 + l32) * QSTR + ks * 16 + half * 8));
+      const int rbase = c0 + rb * 32 + 4 * half;
+      float lse[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lse[r] = sL[rbase + 8 * (r / 4) + (r % 4)];
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) s = mfma32(af[ks], kf[kg][ks], s);
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc += fast_exp2(fmaf(s[r], p.scale_log2, -lse[r]));
+        col[kg] += acc;
+      }
+    }
+  }
+#pragma unroll
+  for (int kg = 0; kg < 2; ++kg) {
+    const float tot = col[kg] + swap_half(col[kg]);
+    if (half == 0 && key[kg] < hi) p.scores[(int64_t)g * p.n_tokens + key[kg]] = tot;
+  }
+}
+
+// ------------------------------------------------------------------ 3. top-l_p selection
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(kThreads) void select_topk(const ScoreParams p) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_prefix, sh_need;
+  __shared__ uint32_t wave_cnt[2][kThreads / 64];
+
+  const int v = blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
+  const int lo = p.bs[v], hi = p.bs[v + 1];
+  const float* sc = p.scores + (int64_t)g * p.n_tokens;
+  int32_t* out = p.sel + ((int64_t)v * p.hkv + g) * p.l_pass;
+  if (p.l_pass == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // radix select, most significant byte first: find the exact l_pass-th largest key
+  uint32_t prefix = 0, need = (uint32_t)p.l_pass;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+    hist[tid] = 0;
+    __syncthreads();
+    for (int j = lo + tid; j < hi; j += kThreads) {
+      const uint32_t k = order_key(sc[j]);
+      if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t acc = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (acc + hist[d] >= need) break;
+        acc += hist[d];
+      }
+      sh_prefix = prefix | ((uint32_t)d << shift);
+      sh_need = need - acc;
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    need = sh_need;
+    __syncthreads();
+  }
+  // prefix = threshold key T; take every key > T and the first `need` keys == T (by row)
+  const uint32_t T = prefix;
+  uint32_t base_sel = 0, base_eq = 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int j0 = lo; j0 < hi; j0 += kThreads) {
+    const int j = j0 + tid;
+    const uint32_t k = j < hi ? order_key(sc[j]) : 0u;
+    const bool eq = j < hi && k == T;
+    const uint64_t eq_b = __ballot(eq);
+    __syncthreads();
+    if (lane == 0) wave_cnt[0][wave] = __popcll(eq_b);
+    __syncthreads();
+    uint32_t eq_before = base_eq;
+    for (int w = 0; w < wave; ++w) eq_before += wave_cnt[0][w];
+    eq_before += __popcll(eq_b & lt_mask);
+    const bool take = j < hi && (k > T || (eq && eq_before < need));
+    const uint64_t tk_b = __ballot(take);
+    if (lane == 0) wave_cnt[1][wave] = __popcll(tk_b);
+    __syncthreads();
+    uint32_t pos = base_sel;
+    for (int w = 0; w < wave; ++w) pos += wave_cnt[1][w];
+    pos += __popcll(tk_b & lt_mask);
+    if (take) out[pos] = j;
+    uint32_t tot_eq = 0, tot_sel = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      tot_eq += wave_cnt[0][w];
+      tot_sel += wave_cnt[1][w];
+    }
+    base_eq += tot_eq;
+    base_sel += tot_sel;
+  }
+}
+
+}  // namespace
+
+size_t score_workspace_bytes(int n_blocks, int hkv, int rows, int n_split, int n_tokens,
+                             bool need_scores) {
+  size_t stats = (size_t)n_blocks * hkv * n_split * rows * sizeof(float2);
+  stats = (stats + 255) & ~(size_t)255;
+  const size_t sc = need_scores ? (size_t)hkv * n_tokens * sizeof(float) : 0;
+  return stats + sc;
+}
+
+hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block,
+                               hipStream_t stream) {
+  const int n_rg = (p.rows + 127) / 128;
+  if (p.rows > 0) {
+    dim3 grid(p.n_blocks * p.hkv * n_rg * p.n_split);
+    if (head_dim == 128)
+      hipLaunchKernelGGL(score_rowstats<128>, grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(score_rowstats<64>, grid, dim3(kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int n_kt = (max_block + kColKeys - 1) / kColKeys;
+    const int rows_pad = ((p.rows + kQChunk - 1) / kQChunk) * kQChunk;
+    const size_t shm = (size_t)kQChunk * (head_dim + 8) * 2 + (size_t)(rows_pad > 0 ? rows_pad : 1) * 4;
+    dim3 grid(p.n_blocks * p.hkv * n_kt);
+    if (head_dim == 128)
+      hipLaunchKernelGGL(score_colsum<128>, grid, dim3(kThreads), shm, stream, p, rows_pad);
+    else
+      hipLaunchKernelGGL(score_colsum<64>, grid, dim3(kThreads), shm, stream, p, rows_pad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.l_pass > 0) {
+    hipLaunchKernelGGL(select_topk, dim3(p.n_blocks * p.hkv), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace apbv

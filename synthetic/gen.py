@@ -89,12 +89,23 @@ def _normal(rng, shape, scale=1.0):
     return x
 
 
-def generate(w: Workload, *, keep_raw: bool = False, seed: int | None = None) -> Inputs:
+def generate(w: Workload, *, keep_raw: bool = False, seed: int | None = None,
+             block_starts=None) -> Inputs:
+    """Draw every input of workload ``w``. ``block_starts`` overrides the block layout (any
+    strictly increasing offsets from 0 to N) for test cases with ragged blocks."""
     rng = np.random.default_rng(w.seed if seed is None else seed)
     N, hq, hkv, d = w.total_tokens, w.hq, w.hkv, w.head_dim
 
     frame_lengths = None
-    if w.frame_range:
+    if block_starts is not None:
+        block_starts = np.asarray(block_starts, np.int32)
+        if block_starts[0] != 0 or block_starts[-1] != N or np.any(np.diff(block_starts) <= 0):
+            raise ValueError("block_starts must increase strictly from 0 to N")
+        if w.keys == "frame":
+            F = math.ceil(N / w.frame_len)
+            frame_lengths = np.full(F, w.frame_len, np.int64)
+            frame_lengths[-1] = N - w.frame_len * (F - 1)
+    elif w.frame_range:
         lo, hi = w.frame_range
         draw = rng.integers(lo, hi + 1, size=math.ceil(N / lo) + 1)
         cum = np.cumsum(draw)

@@ -1,0 +1,179 @@
+"""C-ABI library: loads, exports what include/apbv.h declares, rejects bad arguments on the
+host before any launch, and builds a ZigZag schedule with the balance the method claims
+(CPU only: no kernel is launched here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sequence_approximate_attention_score_amd as apbv
+from sequence_approximate_attention_score_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "apbv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(apbv_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = apbv.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTED)
+    assert apbv.version().startswith("apbv-gfx950")
+
+
+def small_layout(**kw):
+    args = dict(block_starts=[0, 300, 600, 900], l_anchor=64, l_query=32, l_pass=32, hq=4, hkv=2,
+                head_dim=128)
+    args.update(kw)
+    return apbv.Layout(args.pop("block_starts"), **args)
+
+
+class FakePtr:
+    """Stands in for a tensor: only data_ptr() is used by the binding's validation path."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def call_attn(layout, **ptrs):
+    p = dict(q=0x1000, kp=0x2000, vp=0x3000, kc=0x4000, vc=0x5000, out=0x6000, lse=None)
+    p.update(ptrs)
+    return apbv.lib().apbv_approx_attn_prefill(layout.ref(), p["q"], p["kp"], p["vp"], p["kc"],
+                                               p["vc"], p["out"], p["lse"], ptrs.get("rb", 0),
+                                               ptrs.get("re", 0), None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(block_starts=[0, 300, 300, 900]), _lib.APBV_EINVAL),     # empty block
+    (dict(block_starts=[5, 300, 600]), _lib.APBV_EINVAL),          # does not start at 0
+    (dict(hq=6, hkv=4), _lib.APBV_EINVAL),                          # hq % hkv != 0
+    (dict(head_dim=96), _lib.APBV_EUNSUPPORTED),                    # unsupported d
+    (dict(l_pass=301), _lib.APBV_EINVAL),                           # l_pass > shortest block
+    (dict(l_anchor=-1), _lib.APBV_EINVAL),
+    (dict(scale=float("inf")), _lib.APBV_EINVAL),
+    (dict(q_row_stride=100), _lib.APBV_EINVAL),                     # stride < hq*d
+    (dict(kv_row_stride=260), _lib.APBV_EINVAL),                    # not a multiple of 8
+    (dict(block_starts=list(range(0, 66 * 8, 8))), _lib.APBV_EINVAL),  # > 64 blocks
+])
+def test_invalid_layouts_are_rejected_before_launch(bad, code):
+    lay = small_layout(**bad)
+    assert call_attn(lay) == code
+    assert apbv.lib().apbv_last_error().decode() != ""
+    assert apbv.lib().apbv_num_buckets(lay.ref()) == -1
+
+
+def test_invalid_pointers_and_ranges():
+    lay = small_layout()
+    assert call_attn(lay, q=None) == _lib.APBV_EINVAL
+    assert call_attn(lay, out=0x6008) == _lib.APBV_EINVAL           # misaligned
+    assert call_attn(lay, lse=0x7002) == _lib.APBV_EINVAL
+    assert call_attn(lay, rb=0, re=3) == _lib.APBV_EINVAL           # 2 buckets only
+    assert call_attn(lay, rb=2, re=1) == _lib.APBV_EINVAL
+    L = apbv.lib()
+    ws = ctypes.c_size_t(0)
+    assert L.apbv_score_select_workspace(lay.ref(), ctypes.byref(ws)) == 0 and ws.value > 0
+    # workspace too small -> EWORKSPACE, without launching anything
+    st = L.apbv_score_select(lay.ref(), 0x1000, 0x2000, None, 0x3000, 0x4000, 16, None)
+    assert st == _lib.APBV_EWORKSPACE
+    st = L.apbv_score_select(lay.ref(), 0x1000, 0x2000, None, 0x3000, None, 0, None)
+    assert st == _lib.APBV_EWORKSPACE
+    st = L.apbv_gather_passing(lay.ref(), 0x1000, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None)
+    assert st == _lib.APBV_EINVAL                                   # v_anchor missing
+    assert L.apbv_approx_attn_prefill(None, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == _lib.APBV_EINVAL
+    assert L.apbv_status_str(3).decode().startswith("workspace")
+
+
+def rows_per_tile():
+    return apbv.attn_tile_rows(128)
+
+
+def unit_pairs(layout):
+    u = apbv.schedule(layout)
+    parts = []
+    for a, ta, b, tb in u:
+        parts.append([(int(a), int(ta))] if a >= 0 else [])
+        if b >= 0:
+            parts[-1].append((int(b), int(tb)))
+    return parts
+
+
+@pytest.mark.parametrize("bs", [[0, 1024, 2048, 3072, 4096], [0, 1000, 2100, 3000],
+                                [0, 777], [0, 128, 256, 384, 512, 640]])
+@pytest.mark.parametrize("zigzag", [0, 1])
+def test_schedule_covers_every_tile_once(bs, zigzag):
+    lay = small_layout(block_starts=bs, l_pass=0, zigzag=zigzag)
+    T = rows_per_tile()
+    seen = []
+    for parts in unit_pairs(lay):
+        assert 1 <= len(parts) <= 2
+        seen += parts
+    want = [(v, t) for v in range(len(bs) - 1) for t in range(-(-(bs[v + 1] - bs[v]) // T))]
+    assert sorted(seen) == sorted(want)
+
+
+def unit_keys(layout, parts):
+    """(row, key) pairs of a unit counted from the mask definition (anchor + passing prefix
+    of earlier blocks + causal local keys), summed over the unit's parts."""
+    T = rows_per_tile()
+    tot = 0
+    for v, t in parts:
+        lo, hi = layout.block_starts[v], layout.block_starts[v + 1]
+        r0, r1 = lo + t * T, min(lo + (t + 1) * T, hi)
+        for i in range(r0, r1):
+            tot += layout.l_anchor + v * layout.l_pass + (i - lo + 1)
+    return tot
+
+
+def test_zigzag_units_carry_equal_work():
+    """ZigZag pairing of blocks p and n-1-p: each bucket's passing length is (n-1)*l_p
+    (equal for all buckets), and with equal blocks every unit holds the same number of
+    (row, key) pairs; block order does not balance."""
+    T = rows_per_tile()
+    n, Lb = 8, 4 * T
+    bs = [v * Lb for v in range(n + 1)]
+    lay = small_layout(block_starts=bs, l_anchor=96, l_pass=40, zigzag=1)
+    work = [unit_keys(lay, p) for p in unit_pairs(lay)]
+    assert len(set(work)) == 1, work
+    for b in range(apbv.num_buckets(lay)):
+        assert (b + (n - 1 - b)) * lay.l_pass == (n - 1) * lay.l_pass
+    flat = small_layout(block_starts=bs, l_anchor=96, l_pass=40, zigzag=0)
+    fw = [unit_keys(flat, p) for p in unit_pairs(flat)]
+    assert max(fw) > 2 * min(fw)
+    # per-bucket totals equal too (the method's balance across physical hosts)
+    per_bucket = [sum(unit_keys(lay, p) for p in unit_pairs_range(lay, b)) for b in range(n // 2)]
+    assert len(set(per_bucket)) == 1
+
+
+def unit_pairs_range(layout, b):
+    u = apbv.schedule(layout, b, b + 1)
+    out = []
+    for a, ta, c, tc in u:
+        parts = [(int(a), int(ta))] if a >= 0 else []
+        if c >= 0:
+            parts.append((int(c), int(tc)))
+        out.append(parts)
+    return out
+
+
+def test_schedule_ranges_partition_the_units():
+    lay = small_layout(block_starts=[0, 500, 1000, 1600, 2000, 2600], zigzag=1)
+    nb = apbv.num_buckets(lay)
+    assert nb == 3
+    full = apbv.schedule(lay)
+    parts = np.concatenate([apbv.schedule(lay, b, b + 1) for b in range(nb)])
+    assert np.array_equal(full, parts)

@@ -1,0 +1,263 @@
+"""HIP path against the oracle, through the C ABI, on seeded synthetic inputs (needs a GPU).
+
+Small cases compare every element; the full-size workloads (64K-256K tokens, the launch
+configuration the benchmark times) compare sampled blocks (scores and selection, computed
+whole by the oracle) and sampled rows (attention, computed row by row by the oracle).
+Attention is teacher-forced: the oracle's attention runs on the prefix gathered from the
+GPU's own selection, so a near-tie difference in selection cannot leak into the attention
+comparison; where the two selections agree the end-to-end outputs are compared too.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from synthetic import generate, workload
+from gpu_util import (check_attention, check_selection, dev_bf16, host_f64, layout_of, say,
+                      upload)
+import sequence_approximate_attention_score_amd as apbv
+from oracle import apbv_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    apbv.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_gpu(x, lay, d):
+    scores, sel = apbv.score_select(lay, d["q_query"], d["k_ctx"])
+    k_pre, v_pre = apbv.gather_passing(lay, d["k_anchor"], d["v_anchor"], d["k_ctx"], d["v_ctx"], sel)
+    out, lse = apbv.approx_attn_prefill(lay, d["q_ctx"], k_pre, v_pre, d["k_ctx"], d["v_ctx"],
+                                        want_lse=True)
+    torch.cuda.synchronize()
+    return dict(scores=scores.cpu().numpy(), sel=sel.cpu().numpy(), k_pre=host_f64(k_pre),
+                v_pre=host_f64(v_pre), out=host_f64(out), lse=lse.cpu().numpy().astype(np.float64))
+
+
+def check_scores(s_gpu, s_or, blocks, bs, G, l_q):
+    for v in blocks:
+        lo, hi = bs[v], bs[v + 1]
+        a, b = s_gpu[:, lo:hi].astype(np.float64), s_or[:, lo:hi]
+        rel = np.abs(a - b) / np.maximum(np.abs(b), 1e-30)
+        say(f"  scores block {v}: max rel err {rel.max():.2e}")
+        # fp32 accumulation of G*l_q probabilities from bf16 MFMA logits
+        assert rel.max() <= 2e-5, (v, rel.max())
+        assert np.allclose(a.sum(axis=1), G * l_q, rtol=1e-5)
+
+
+def full_check(x, lay, *, rows=None, heads=None, blocks=None):
+    """Run the GPU path, then compare scores / selection / gather / attention to the oracle.
+    Every sub-check runs and reports before the first failure is raised."""
+    w = x.w
+    bs = np.asarray(lay.block_starts)
+    say(f"case {w.name}: n={lay.n_blocks} N={lay.n_tokens} hq={w.hq} hkv={w.hkv} d={w.head_dim} "
+        f"l_a={lay.l_anchor} l_q={w.l_query} l_p={lay.l_pass} zigzag={lay.c.zigzag}")
+    d = upload(x)
+    g = run_gpu(x, lay, d)
+    qq, kc, vc = x.f32("q_query"), x.f32("k_ctx"), x.f32("v_ctx")
+    ka, va, qc = x.f32("k_anchor")[:lay.l_anchor], x.f32("v_anchor")[:lay.l_anchor], x.f32("q_ctx")
+    blocks = range(lay.n_blocks) if blocks is None else blocks
+    failures = []
+
+    def attempt(name, fn):
+        try:
+            fn()
+        except AssertionError as e:
+            say(f"  FAILED {name}: {e}")
+            failures.append(name)
+
+    s_or = orc.passing_scores(qq, kc, bs, w.hq, w.hkv, 1 / math.sqrt(w.head_dim), blocks=blocks)
+    attempt("scores", lambda: check_scores(g["scores"], s_or, blocks, bs, w.hq // w.hkv, w.l_query))
+    s32 = s_or.astype(np.float32)
+
+    def sel_check():
+        n_band = sum(_sel_one(s32, g["sel"], bs, lay.l_pass, v) for v in blocks)
+        say(f"  selection: equal outside the tie band ({n_band} band positions)")
+    attempt("selection", sel_check)
+    # gather: bitwise against the oracle's gather of the GPU's own selection
+    kp, vp = orc.gather_prefix(ka, va, kc, vc, g["sel"])
+
+    def gather_check():
+        assert np.array_equal(g["k_pre"], kp) and np.array_equal(g["v_pre"], vp), "gather"
+    attempt("gather", gather_check)
+    # attention, teacher-forced on the GPU selection
+    o_or, l_or = orc.attend(qc, kp, vp, kc, vc, bs, lay.l_anchor, lay.l_pass, w.hq, w.hkv,
+                            1 / math.sqrt(w.head_dim), rows=rows, heads=heads)
+    attempt("attention", lambda: check_attention(g["out"], o_or, "attention out"))
+
+    def lse_check():
+        m = ~np.isnan(l_or)
+        lerr = np.abs(g["lse"][m] - l_or[m]).max()
+        say(f"  lse: max-abs {lerr:.2e}")
+        assert lerr <= 2e-3, lerr
+    attempt("lse", lse_check)
+    assert not failures, failures
+    return g, s_or
+
+
+def _sel_one(s32, sel, bs, l_pass, v):
+    """Selection rule on block v alone (shifted to look like block 0 of one block)."""
+    lo, hi = int(bs[v]), int(bs[v + 1])
+    return check_selection(s32[:, lo:hi], sel[v:v + 1] - lo, [0, hi - lo], l_pass)
+
+
+def small(name="c0", **kw):
+    return generate(workload(name, **kw))
+
+
+# ------------------------------------------------------------------------- small, exhaustive
+def test_c0_end_to_end():
+    x = small("c0")
+    lay = layout_of(x)
+    g, s_or = full_check(x, lay)
+    sel_or = orc.select_passing(s_or.astype(np.float32), x.block_starts, lay.l_pass)
+    if np.array_equal(sel_or, g["sel"]):
+        ref = orc.approx_attention_prefill(x.f32("q_query"), x.f32("q_ctx"), x.f32("k_ctx"),
+                                           x.f32("v_ctx"), x.f32("k_anchor"), x.f32("v_anchor"),
+                                           x.block_starts, lay.l_pass, 2, 1, 1 / 8)
+        check_attention(g["out"], ref["out"], "end-to-end out")
+
+
+VARIANTS = {
+    # name: (workload overrides, explicit block_starts or None, layout overrides)
+    "ragged_odd_n_g7": (dict(hq=14, hkv=2, head_dim=128, total_tokens=1000, l_anchor=37,
+                             l_query=19, l_pass=21), [0, 129, 300, 555, 700, 1000], {}),
+    "no_anchor": (dict(hq=4, hkv=2, head_dim=128, total_tokens=900, l_anchor=0, l_query=16,
+                       l_pass=40), [0, 300, 600, 900], {}),
+    "no_passing": (dict(hq=4, hkv=4, head_dim=64, total_tokens=700, l_anchor=50, l_query=8,
+                        l_pass=0), [0, 350, 700], {}),
+    "lp_equals_block": (dict(hq=2, hkv=1, head_dim=64, total_tokens=384, l_anchor=16,
+                             l_query=4, l_pass=128), [0, 128, 256, 384], {}),
+    "single_query_row": (dict(hq=7, hkv=1, head_dim=128, total_tokens=600, l_anchor=64,
+                              l_query=1, l_pass=33), [0, 200, 400, 600], {}),
+    "tiny_blocks": (dict(hq=2, hkv=1, head_dim=64, total_tokens=40, l_anchor=3, l_query=3,
+                         l_pass=1), [0, 5, 13, 14, 40], {}),
+    "many_blocks_zigzag_off": (dict(hq=4, hkv=1, head_dim=128, total_tokens=64 * 40,
+                                    l_anchor=8, l_query=8, l_pass=8),
+                               list(range(0, 64 * 40 + 1, 40)), dict(zigzag=False)),
+    "big_query_block": (dict(hq=4, hkv=2, head_dim=128, total_tokens=2500, l_anchor=100,
+                             l_query=300, l_pass=64), [0, 1200, 2500], {}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
+def test_variant(name):
+    wkw, bs, lkw = VARIANTS[name]
+    x = generate(dataclasses.replace(workload("c0"), name=name, keys="iid", block_len=0,
+                                     n_blocks=len(bs) - 1, **wkw), block_starts=bs)
+    lay = layout_of(x, **lkw)
+    full_check(x, lay)
+
+
+def test_single_block_is_dense_causal():
+    """n = 1, no prefix: the kernel is plain causal attention (checked against the oracle,
+    whose own pin ties this case to torch's causal SDPA)."""
+    x = generate(dataclasses.replace(workload("c0"), name="dense", hq=8, hkv=2, head_dim=128,
+                                     total_tokens=1500, n_blocks=1, block_len=1500, l_anchor=0,
+                                     l_query=4, l_pass=0))
+    lay = layout_of(x)
+    full_check(x, lay)
+
+
+def test_fused_qkv_strides():
+    """q_ctx / k_ctx / v_ctx as views into one fused [N, (hq + 2 hkv) d] buffer."""
+    x = small("c0", hq=4, hkv=2, head_dim=128, total_tokens=700, n_blocks=2, block_len=350,
+              l_anchor=32, l_query=16, l_pass=24)
+    w = x.w
+    N, d = x.N, w.head_dim
+    fused = np.concatenate([x.bits["q_ctx"].reshape(N, -1), x.bits["k_ctx"].reshape(N, -1),
+                            x.bits["v_ctx"].reshape(N, -1)], axis=1)
+    F = dev_bf16(fused)
+    stride = F.shape[1]
+    qv = F[:, : w.hq * d]
+    kv = F[:, w.hq * d: (w.hq + w.hkv) * d]
+    vv = F[:, (w.hq + w.hkv) * d:]
+    lay = layout_of(x, q_row_stride=stride, kv_row_stride=stride)
+    dd = upload(x, ("q_query", "k_anchor", "v_anchor"))
+    _, sel = apbv.score_select(lay, dd["q_query"], kv)
+    kp, vp = apbv.gather_passing(lay, dd["k_anchor"], dd["v_anchor"], kv, vv, sel)
+    out, _ = apbv.approx_attn_prefill(lay, qv, kp, vp, kv, vv)
+    ref_lay = layout_of(x)
+    d2 = upload(x)
+    ref = run_gpu(x, ref_lay, d2)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), ref["sel"])
+    assert np.array_equal(host_f64(out), ref["out"])
+
+
+def test_zigzag_ranges_and_determinism():
+    """Same bits with and without ZigZag, run twice, and bucket by bucket."""
+    x = small("c0", hq=4, hkv=2, head_dim=128, total_tokens=6 * 300, n_blocks=6, block_len=300,
+              l_anchor=40, l_query=16, l_pass=30)
+    d = upload(x)
+    a = run_gpu(x, layout_of(x, zigzag=True), d)
+    b = run_gpu(x, layout_of(x, zigzag=False), d)
+    c = run_gpu(x, layout_of(x, zigzag=True), d)
+    for k in ("scores", "sel", "k_pre", "out", "lse"):
+        assert np.array_equal(a[k], b[k]), k
+        assert np.array_equal(a[k], c[k]), k
+    lay = layout_of(x, zigzag=True)
+    _, sel = apbv.score_select(lay, d["q_query"], d["k_ctx"])
+    kp, vp = apbv.gather_passing(lay, d["k_anchor"], d["v_anchor"], d["k_ctx"], d["v_ctx"], sel)
+    out = torch.zeros((x.N, 4, 128), dtype=torch.bfloat16, device="cuda")
+    for bkt in range(apbv.num_buckets(lay)):
+        apbv.approx_attn_prefill(lay, d["q_ctx"], kp, vp, d["k_ctx"], d["v_ctx"], out=out,
+                                 range_begin=bkt, range_end=bkt + 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f64(out), a["out"])
+
+
+# ------------------------------------------------------------------------- full size, sampled
+def sample_rows(bs, tile, rng, per_block=24):
+    rows = []
+    for v in range(len(bs) - 1):
+        lo, hi = int(bs[v]), int(bs[v + 1])
+        pick = {lo, lo + 1, hi - 1, hi - 2, min(lo + tile - 1, hi - 1), min(lo + tile, hi - 1)}
+        pick |= set(int(r) for r in rng.integers(lo, hi, per_block))
+        rows += sorted(pick)
+    return np.asarray(sorted(set(rows)))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_full_size_sampled(name):
+    x = generate(workload(name))
+    w = x.w
+    lay = layout_of(x)
+    bs = x.block_starts
+    rng = np.random.default_rng(7)
+    rows = sample_rows(bs, apbv.attn_tile_rows(w.head_dim), rng)
+    heads = [0, w.hq // 2, w.hq - 1]
+    blocks = sorted({0, lay.n_blocks // 2, lay.n_blocks - 1})
+    full_check(x, lay, rows=rows, heads=heads, blocks=blocks)
+
+
+def test_dense_causal_128k_sampled():
+    """Dense causal attention over [anchor | 128K context] (n = 1, no prefix): the
+    comparison the frame-balanced 128K workload reports, on sampled rows."""
+    w = workload("c4")
+    x = generate(w)
+    N = x.N + w.l_anchor
+    lay = apbv.Layout([0, N], l_anchor=0, l_query=0, l_pass=0, hq=w.hq, hkv=w.hkv,
+                      head_dim=w.head_dim)
+    q = np.concatenate([x.bits["q_anchor"], x.bits["q_ctx"]])
+    k = np.concatenate([x.bits["k_anchor"], x.bits["k_ctx"]])
+    v = np.concatenate([x.bits["v_anchor"], x.bits["v_ctx"]])
+    dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    out, lse = apbv.approx_attn_prefill(lay, dq, None, None, dk, dv, want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.asarray(sorted({0, 1, 127, 128, N - 1} | set(np.random.default_rng(3).integers(0, N, 40).tolist())))
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    o_or, l_or = orc.attend(f(q), np.zeros((w.hkv, 0, w.head_dim)), np.zeros((w.hkv, 0, w.head_dim)),
+                            f(k), f(v), [0, N], 0, 0, w.hq, w.hkv, 1 / math.sqrt(w.head_dim),
+                            rows=rows, heads=[0, 27])
+    check_attention(host_f64(out), o_or, "dense causal 128K")

@@ -31,11 +31,11 @@ MUTATIONS = {
     "anchor dropped from the visible prefix":
         ("P = l_anchor + v * l_pass\n", "P = l_anchor + v * l_pass\n        kp = kp[:, l_anchor:]; vp = vp[:, l_anchor:]; P -= l_anchor\n"),
     "attention scale dropped":
-        ("z = scale * (q[r, h, :] @ keys.T)", "z = (q[r, h, :] @ keys.T)"),
+        ("z = scale * (_as64(q_ctx[r, h, :]) @ keys.T)", "z = (_as64(q_ctx[r, h, :]) @ keys.T)"),
     "score softmax over the queries instead of the keys":
         ("s[g, lo:hi] += _softmax_rows(z).sum(axis=0)", "s[g, lo:hi] += _softmax_rows(z.T).sum(axis=1)"),
     "score scale dropped":
-        ("z = scale * (q[:, h, :] @ k[lo:hi, g, :].T)", "z = (q[:, h, :] @ k[lo:hi, g, :].T)"),
+        ("z = scale * (q[:, h, :] @ k[:, g, :].T)", "z = (q[:, h, :] @ k[:, g, :].T)"),
     "ties go to the higher position":
         ('order = np.argsort(-s[g, lo:hi], kind="stable")',
          'order = (hi - lo - 1) - np.argsort(-s[g, lo:hi][::-1], kind="stable")'),
@@ -46,11 +46,11 @@ MUTATIONS = {
     "lse without the log":
         ("lse[h, r] = (m + np.log(l))[:, 0]", "lse[h, r] = (m + l)[:, 0]"),
     "values gathered from the keys":
-        ("v_parts = [va[:, g, :]] + [vc[sel[v, g], g, :] for v in range(n)]",
-         "v_parts = [va[:, g, :]] + [kc[sel[v, g], g, :] for v in range(n)]"),
+        ("v_parts = [va[:, g, :]] + [_as64(vc[sel[v, g], g, :]) for v in range(n)]",
+         "v_parts = [va[:, g, :]] + [_as64(kc[sel[v, g], g, :]) for v in range(n)]"),
     "passing rows off by one":
-        ("k_parts = [ka[:, g, :]] + [kc[sel[v, g], g, :] for v in range(n)]",
-         "k_parts = [ka[:, g, :]] + [kc[np.minimum(sel[v, g] + 1, kc.shape[0] - 1), g, :] for v in range(n)]"),
+        ("k_parts = [ka[:, g, :]] + [_as64(kc[sel[v, g], g, :]) for v in range(n)]",
+         "k_parts = [ka[:, g, :]] + [_as64(kc[np.minimum(sel[v, g] + 1, kc.shape[0] - 1), g, :]) for v in range(n)]"),
     "softmax without normalisation":
         ("return e / np.sum(e, axis=-1, keepdims=True)", "return e"),
     "selection indices relative to the block":
