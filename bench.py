@@ -1,0 +1,234 @@
+"""Benchmark of the approximate-attention prefill hot path on one MI355X.
+
+One step = one layer of the hot path on the 128K-token Qwen2.5-VL-7B-shaped workload
+(28 query / 4 KV heads, head_dim 128, 16 virtual blocks of 8K on 8 ZigZag buckets,
+anchor 2048, query block 128, l_p 1024): score_select -> gather_passing ->
+approx_attn_prefill, with every input already resident in HBM. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+                    [--profile] [--calib-copy]
+
+``--profile`` shortens the run for rocprofv3 (no CPU baseline); ``--calib-copy`` also runs
+a plain 1 GiB device copy so that HBM byte counters can be scaled against a known size.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "approx-attn prefill tokens/s per layer at 128K ctx; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+ATTN_SOURCES = ["sequence_approximate_attention_score_amd/csrc/attn.hip",
+                "sequence_approximate_attention_score_amd/csrc/apbv_device.h",
+                "sequence_approximate_attention_score_amd/csrc/apbv_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_c2_traffic.txt")
+
+
+def attention_flops(block_starts, l_anchor, l_pass, hq, d) -> float:
+    """Algorithmic attention FLOPs: 4*d per visible (row, key) pair per query head."""
+    pairs = 0
+    for v in range(len(block_starts) - 1):
+        L = int(block_starts[v + 1] - block_starts[v])
+        P = l_anchor + v * l_pass
+        pairs += L * P + L * (L + 1) // 2
+    return float(pairs) * hq * 4 * d
+
+
+def attn_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None
+    if it is missing or was taken on a different attention kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != attn_source_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, budget_s: float = 15.0):
+    """The float64 oracle, as it is, on a bounded sample of the same workload: scores and
+    selection of the middle block for every KV head, and the attention of that block for as
+    many query heads as fit in about ``budget_s`` seconds (one per KV group first);
+    extrapolated to the whole layer by algorithmic work."""
+    from oracle import apbv_oracle as orc
+    w = x.w
+    bs = np.asarray(x.block_starts)
+    n = len(bs) - 1
+    v = n // 2
+    scale = 1.0 / math.sqrt(w.head_dim)
+    qq, kc, vc = x.f32("q_query"), x.f32("k_ctx"), x.f32("v_ctx")
+    t0 = time.perf_counter()
+    s = orc.passing_scores(qq, kc, bs, w.hq, w.hkv, scale, blocks=[v])
+    t_score = time.perf_counter() - t0
+    # selection of every block is needed for the prefix; blocks other than v keep the top rows
+    # of their (unscored) keys by position so that the sample stays bounded
+    s32 = np.nan_to_num(s, nan=0.0).astype(np.float32)
+    t1 = time.perf_counter()
+    sel = orc.select_passing(s32, bs, w.l_pass)
+    kp, vp = orc.gather_prefix(x.f32("k_anchor"), x.f32("v_anchor"), kc, vc, sel)
+    t_sel = time.perf_counter() - t1
+    G = w.hq // w.hkv
+    order = [g * G + j for j in range(G) for g in range(w.hkv)]   # one head per group first
+    L = int(bs[v + 1] - bs[v])
+    rows = np.arange(bs[v], bs[v + 1])
+    heads = []
+    t2 = time.perf_counter()
+    for h in order:                        # add heads until about budget_s of CPU work
+        orc.attend(x.f32("q_ctx"), kp, vp, kc, vc, bs, w.l_anchor, w.l_pass, w.hq, w.hkv,
+                   scale, rows=rows, heads=[h])
+        heads.append(h)
+        if time.perf_counter() - t2 >= budget_s:
+            break
+    t_attn = time.perf_counter() - t2
+    P = w.l_anchor + v * w.l_pass
+    sample_pairs = (L * P + L * (L + 1) // 2) * len(heads)
+    total_pairs = attention_flops(bs, w.l_anchor, w.l_pass, 1, 1) / 4
+    est = t_score * n + t_sel + t_attn * (total_pairs / sample_pairs)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    return {"value": x.N / est, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"float64 numpy oracle on block {v} of {n}: scores+selection for all "
+                       f"{w.hkv} KV heads ({t_score:.1f}s), gather ({t_sel:.1f}s), attention of "
+                       f"{len(heads)} of {w.hq} heads over the block's {L} rows ({t_attn:.1f}s); "
+                       f"layer time extrapolated by block count (scores) and by visible "
+                       f"(row, key) pairs (attention): {est:.0f}s per layer")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the approximate-attention path is built for a single "
+              "MI355X (all virtual blocks on one device, no collectives); runs on more than one "
+              "GPU are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sequence_approximate_attention_score_amd as apbv
+    from synthetic import generate, workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = workload(args.workload)
+    print(f"# generating {w.name}: {w.description}", file=sys.stderr, flush=True)
+    x = generate(w)
+    up = lambda n: torch.from_numpy(x.bits[n].view(np.int16)).to(dev).view(torch.bfloat16)
+    d = {n: up(n) for n in ("q_query", "q_ctx", "k_ctx", "v_ctx", "k_anchor", "v_anchor")}
+    lay = apbv.Layout(x.block_starts, l_anchor=w.l_anchor, l_query=w.l_query, l_pass=w.l_pass,
+                      hq=w.hq, hkv=w.hkv, head_dim=w.head_dim, zigzag=True)
+    ws = torch.empty(max(apbv.score_select_workspace(lay), 256), dtype=torch.uint8, device=dev)
+    sel = torch.empty((lay.n_blocks, w.hkv, w.l_pass), dtype=torch.int32, device=dev)
+    kp = torch.empty((w.hkv, lay.pre_rows, w.head_dim), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    out = torch.empty((x.N, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        apbv.score_select(lay, d["q_query"], d["k_ctx"], sel=sel, workspace=ws, want_scores=False)
+        if ev is not None:
+            ev[1].record()
+        apbv.gather_passing(lay, d["k_anchor"], d["v_anchor"], d["k_ctx"], d["v_ctx"], sel,
+                            k_pre=kp, v_pre=vp)
+        if ev is not None:
+            ev[2].record()
+        apbv.approx_attn_prefill(lay, d["q_ctx"], kp, vp, d["k_ctx"], d["v_ctx"], out=out)
+        if ev is not None:
+            ev[3].record()
+
+    steps, warmup = (3, 1) if args.profile else (args.steps, args.warmup)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                    for e in evs])   # ms: score_select, gather, attention
+    ms_step = (t1 - t0) * 1e3 / steps
+    if args.calib_copy:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    flops = attention_flops(x.block_starts, w.l_anchor, w.l_pass, w.hq, w.head_dim)
+    attn_ms = float(per[:, 2].mean())
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": x.N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: Qwen2.5-VL-7B-shaped layer, {x.N // 1024}K visual tokens",
+                   "tokens": x.N, "virtual_blocks": lay.n_blocks, "zigzag_buckets": w.n_buckets,
+                   "hq": w.hq, "hkv": w.hkv, "head_dim": w.head_dim, "l_anchor": w.l_anchor,
+                   "l_query": w.l_query, "l_pass": w.l_pass},
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel (approx_attn_prefill)",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": read_traffic(),
+                     "algorithmic_flop_per_launch": flops},
+        "breakdown_ms": {"score_select": float(per[:, 0].mean()), "gather": float(per[:, 1].mean()),
+                         "attention": attn_ms},
+        "attention_only_tokens_per_s": x.N / (attn_ms * 1e-3),
+        "cpu_baseline": None,
+    }
+    if not (args.profile or args.no_cpu_baseline):
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
