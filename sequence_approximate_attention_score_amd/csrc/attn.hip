@@ -7,21 +7,29 @@
 // Approssimata"; with one block and no prefix this is plain causal flash attention, as the
 // page's "Limitazioni" paragraph notes).
 //
-// Design (one workgroup = 4 waves = one query tile of 128*RB rows of one head):
+// Design (default variant: one workgroup = 8 waves = one query tile of 256 rows of one head,
+// 32 rows per wave, two waves per SIMD so one wave's softmax overlaps the other's MFMAs):
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: the K tile (shared by the waves) is the A
 //    operand read from LDS, the wave's Q rows are the B operand held in registers. The
 //    result puts one query row per lane (lanes l and l+32 share a row and split its keys),
 //    so row max / sum are lane-local plus one permlane32 swap.
-//  * O^T = V^T . P^T: the probabilities are already laid out as the B operand; V is stored
-//    transposed in LDS (key positions permuted to match the S^T register order), so the
-//    rescale factor of a row is lane-local too.
+//  * O^T = V^T . P^T: the probabilities are already laid out as the B operand; the V^T
+//    operand comes straight from a row-major V tile through ds_read_b64_tr_b16 (two
+//    transposing 8-byte reads per operand), so the rescale factor of a row is lane-local.
+//  * K and V tiles of 64 keys go global -> LDS with global_load_lds_dwordx4 (no register
+//    staging), XOR-swizzled per row so that both read patterns are bank-conflict free;
+//    double-buffered, the next tile's loads in flight while the current one is computed,
+//    one barrier per tile.
 //  * Online softmax in log2 units with a lazy rescale: the running offset is only raised
 //    when a tile's maximum exceeds it by more than 8 (probabilities stay <= 256), which is
-//    exact up to rounding and skips almost every O rescale.
-//  * K/V tiles of 64 keys are double-buffered in LDS; the next tile's global loads are in
-//    flight while the current one is computed; one barrier per tile.
+//    exact up to rounding and skips almost every O rescale. Masking code runs only on
+//    tiles that need it (ragged prefix end, causal diagonal).
 //  * Grid = work units x heads, remapped so each XCD gets a contiguous range: the heads of
 //    one KV group and one unit run side by side on the same XCD and share K/V in its L2.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
 #include "apbv_device.h"
 #include "apbv_internal.h"
 
@@ -29,21 +37,30 @@ namespace apbv {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int KT = 64;             // keys per tile
 constexpr float kLazyTau = 8.0f;   // log2 headroom before the running offset is raised
 
-template <int D>
-struct Tile {
-  static constexpr int KSTR = D + 8;    // K tile row stride (bf16 elements, +16 B pad)
-  static constexpr int VSTR = KT + 8;   // V^T tile row stride
-  static constexpr int KCH = KT * D / 8 / kThreads;          // 16-B K chunks per thread
-  static constexpr int VIT = (KT / 4) * (D / 8);             // 4-key x 8-d V items
-  static constexpr int VPT = (VIT + kThreads - 1) / kThreads;  // V items per thread
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Shape of one kernel variant: NW waves, 32*RB query rows per wave, KT keys per tile.
+template <int D, int NW, int RB, int KT>
+struct Shape {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int M = NW * 32 * RB;           // query rows per tile
+  static constexpr int TILE = KT * D;              // elements per K (or V) tile buffer
+  static constexpr int SEG = TILE * 2 / 1024;      // 1 KB wave-load segments per buffer
+  static constexpr int LOADS = 2 * SEG / NW;       // direct loads per lane per tile (K + V)
+  static_assert((2 * SEG) % NW == 0, "tile must split evenly over the waves");
 };
 
-// Source of one key tile: base row pointer for K and V, row stride, first key, valid rows.
+// LDS layouts (both tiles row-major, KT rows of D bf16, no padding, filled 1 KB per
+// wave-load by global->LDS loads; the 16-byte chunk c of row r sits at position c ^ f(r)):
+//  K: f(r) = r & 7       -> the MFMA A-operand read (8 rows, one chunk) touches 8 chunks.
+//  V: f(r) = 2 * (r & 3) -> the transposing read (4 rows x 2 chunks per 16 lanes) touches 8.
+__device__ __forceinline__ int swz_k(int r) { return r & 7; }
+__device__ __forceinline__ int swz_v(int r) { return 2 * (r & 3); }
+
+// Source of one key tile: base row pointer for K and V, row stride, valid rows (>= 1).
 struct KeySrc {
   const uint16_t* k;
   const uint16_t* v;
@@ -51,73 +68,141 @@ struct KeySrc {
   int valid;
 };
 
-template <int D>
-struct Stage {
-  u32x4 k[Tile<D>::KCH];
-  u32x4 v[Tile<D>::VPT][4];
-};
-
-template <int D>
-__device__ __forceinline__ void stage_load(Stage<D>& st, const KeySrc& src) {
-  const int tid = threadIdx.x;
+// K and V tile -> LDS, no registers involved. Rows past `valid` repeat the last valid row;
+// those keys are masked in the scores, so their values only need to be finite.
+template <int D, int NW, int RB, int KT>
+__device__ __forceinline__ void load_tile(uint16_t* sK, uint16_t* sV, const KeySrc& src) {
+  using S = Shape<D, NW, RB, KT>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < Tile<D>::KCH; ++j) {
-    const int c = tid + j * kThreads;
-    const int row = c / (D / 8), col = c % (D / 8);
-    st.k[j] = row < src.valid ? load16(src.k + row * src.stride + col * 8) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int j = 0; j < Tile<D>::VPT; ++j) {
-    const int it = tid + j * kThreads;
-    const int kg = it / (D / 8), dg = it % (D / 8);
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int row = kg * 4 + y;
-      st.v[j][y] = (it < Tile<D>::VIT && row < src.valid)
-                       ? load16(src.v + row * src.stride + dg * 8)
-                       : u32x4{0, 0, 0, 0};
-    }
+  for (int j = 0; j < S::LOADS; ++j) {
+    const int seg = j * NW + wave;                       // 0 .. 2*SEG-1 (K first, then V)
+    const bool is_v = seg >= S::SEG;
+    const int sg = is_v ? seg - S::SEG : seg;
+    const int e = sg * 512 + lane * 8;                   // element this lane fills
+    const int r = e / D, pos = (e % D) / 8;
+    const int c = pos ^ (is_v ? swz_v(r) : swz_k(r));    // logical chunk stored at `pos`
+    const int rr = min(r, src.valid - 1);
+    const uint16_t* g = (is_v ? src.v : src.k) + rr * src.stride + c * 8;
+    __builtin_amdgcn_global_load_lds(g, (is_v ? sV : sK) + sg * 512, 16, 0, 0);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D>& st, uint16_t* sK, uint16_t* sV) {
-  const int tid = threadIdx.x;
+// One key tile for one wave: S^T = K.Q^T, (masked) online softmax, O^T += V^T.P^T.
+template <int D, int RB, int KT, bool MASK>
+__device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* sV,
+                                            const bf16x8 (&qf)[RB][D / 16],
+                                            f32x16 (&o)[RB][D / 32], float (&m_run)[RB],
+                                            float (&l_run)[RB], float scale_log2, bool prefix,
+                                            int key0, int valid, int wrow0) {
+  constexpr int ND = D / 32, NK = D / 16, NN = KT / 32;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const f32x16 zero = {};
+
+  // S^T[key, row] for NN blocks of 32 keys; A = K rows from LDS, B = Q^T from registers
+  f32x16 s[RB][NN];
 #pragma unroll
-  for (int j = 0; j < Tile<D>::KCH; ++j) {
-    const int c = tid + j * kThreads;
-    const int row = c / (D / 8), col = c % (D / 8);
-    store16(sK + row * Tile<D>::KSTR + col * 8, st.k[j]);
+  for (int ks = 0; ks < NK; ++ks) {
+#pragma unroll
+    for (int n = 0; n < NN; ++n) {
+      const int row = n * 32 + l32;
+      const int pos = (2 * ks + half) ^ swz_k(row);
+      const bf16x8 a = as_bf16x8(load16(sK + row * D + pos * 8));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        s[rb][n] = mfma32(a, qf[rb][ks], ks == 0 ? zero : s[rb][n]);
+    }
   }
+
 #pragma unroll
-  for (int j = 0; j < Tile<D>::VPT; ++j) {
-    const int it = tid + j * kThreads;
-    if (it < Tile<D>::VIT) {
-      const int kg = it / (D / 8), dg = it % (D / 8);
-      // keys 4kg..4kg+3 = 16c + 8x + 4b + y sit at V^T positions 16c + 8b + 4x + y
-      const int pos = 16 * (kg / 4) + 8 * (kg % 2) + 4 * ((kg / 2) % 2);
+  for (int rb = 0; rb < RB; ++rb) {
+    if (MASK) {
+      const int row = wrow0 + rb * 32 + l32;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo01 = __builtin_amdgcn_perm(st.v[j][1][w], st.v[j][0][w], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(st.v[j][3][w], st.v[j][2][w], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(st.v[j][1][w], st.v[j][0][w], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(st.v[j][3][w], st.v[j][2][w], 0x07060302u);
-        const int d = dg * 8 + 2 * w;
-        *reinterpret_cast<u32x2*>(sV + d * Tile<D>::VSTR + pos) = u32x2{lo01, lo23};
-        *reinterpret_cast<u32x2*>(sV + (d + 1) * Tile<D>::VSTR + pos) = u32x2{hi01, hi23};
+      for (int n = 0; n < NN; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = n * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+          const bool dead = prefix ? (kk >= valid) : (key0 + kk > row);
+          s[rb][n][r] = dead ? -INFINITY : s[rb][n][r];
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < NN; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][n][r]);
+    mx = fmaxf(mx, swap_half(mx));
+    const float mxs = mx * scale_log2;
+    if (mxs > m_run[rb] + kLazyTau) {
+      if (m_run[rb] != -INFINITY) {     // the first visible tile needs no rescale (O = 0)
+        const float alpha = fast_exp2(m_run[rb] - mxs);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
       }
+      m_run[rb] = mxs;
+    }
+    const float mu = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+    float ls = 0.f;
+#pragma unroll
+    for (int n = 0; n < NN; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(s[rb][n][r], scale_log2, -mu));
+        ls += e;
+        s[rb][n][r] = e;
+      }
+    l_run[rb] += ls;
+  }
+
+  // O^T += V^T . P^T, 16 keys per MFMA. P^T element e of chunk c (lane half h) is key
+  // 16c + 8(e/4) + 4h + e%4 (the S^T register order); the V^T operand is fetched with two
+  // transposing reads: source lane j of each 16-lane group points at key row
+  // 16c + 8t + 4h + j/4 and d columns 32db + 16*(group % 2) + 4*(j % 4) .. +3.
+  const int grp = (lane >> 4) & 1, j16 = lane & 15;
+#pragma unroll
+  for (int c = 0; c < KT / 16; ++c) {
+    bf16x8 pf[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const f32x16& sv = s[rb][c / 2];
+      const int b0 = (c % 2) * 8;
+      u32x4 w = {pack_bf16x2(sv[b0 + 0], sv[b0 + 1]), pack_bf16x2(sv[b0 + 2], sv[b0 + 3]),
+                 pack_bf16x2(sv[b0 + 4], sv[b0 + 5]), pack_bf16x2(sv[b0 + 6], sv[b0 + 7])};
+      pf[rb] = as_bf16x8(w);
+    }
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      s16x4 part[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 16 * c + 8 * t + 4 * half + (j16 >> 2);
+        const int d0 = 32 * db + 16 * grp + 4 * (j16 & 3);
+        const int pos = (d0 >> 3) ^ swz_v(row);
+        const uint16_t* src = sV + row * D + pos * 8 + (d0 & 7);
+        part[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+      }
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
+                          part[1][0], part[1][1], part[1][2], part[1][3]};
+      const bf16x8 va = __builtin_bit_cast(bf16x8, both);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(va, pf[rb], o[rb][db]);
     }
   }
 }
 
-template <int D, int RB>
-__device__ void process_tile(const AttnParams& p, int h, int g, int v, int t, uint16_t* sKbase,
-                             uint16_t* sVbase) {
-  constexpr int M = kWaves * 32 * RB;
+template <int D, int NW, int RB, int KT>
+__device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, int v, int t,
+                                             uint16_t* sKbase, uint16_t* sVbase) {
+  using S = Shape<D, NW, RB, KT>;
+  constexpr int M = S::M;
   constexpr int ND = D / 32;     // 32-wide d blocks of O^T
   constexpr int NK = D / 16;     // 16-deep k steps of S^T
-  constexpr int KSZ = KT * Tile<D>::KSTR;
-  constexpr int VSZ = D * Tile<D>::VSTR;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -126,15 +211,15 @@ __device__ void process_tile(const AttnParams& p, int h, int g, int v, int t, ui
   const int r1 = min(r0 + M, hi);
   const int wrow0 = r0 + wave * 32 * RB;   // first row of this wave
 
-  // Q^T fragments (B operand): lane holds row l32 of each row block, d = 16ks + 8half + e
+  // Q^T fragments (B operand): lane holds row l32 of each row block, d = 16ks + 8half + e.
+  // Rows past the tile end repeat a valid row; their outputs are never stored.
   bf16x8 qf[RB][NK];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int row = wrow0 + rb * 32 + l32;
+    const int row = min(wrow0 + rb * 32 + l32, r1 - 1);
     const uint16_t* qrow = p.q + (int64_t)row * p.q_stride + h * D + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks)
-      qf[rb][ks] = as_bf16x8(row < r1 ? load16(qrow + ks * 16) : u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < NK; ++ks) qf[rb][ks] = as_bf16x8(load16(qrow + ks * 16));
   }
 
   f32x16 o[RB][ND];
@@ -174,105 +259,32 @@ __device__ void process_tile(const AttnParams& p, int h, int g, int v, int t, ui
     return s;
   };
 
-  Stage<D> st;
-  stage_load<D>(st, source(0));
-  stage_store<D>(st, sKbase, sVbase);
+  load_tile<D, NW, RB, KT>(sKbase, sVbase, source(0));
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int i = 0; i < ntiles; ++i) {
     const int buf = i & 1;
-    if (i + 1 < ntiles) stage_load<D>(st, source(i + 1));
-
-    const uint16_t* sK = sKbase + buf * KSZ;
-    const uint16_t* sV = sVbase + buf * VSZ;
+    if (i + 1 < ntiles)
+      load_tile<D, NW, RB, KT>(sKbase + (buf ^ 1) * S::TILE, sVbase + (buf ^ 1) * S::TILE,
+                               source(i + 1));
+    const uint16_t* sK = sKbase + buf * S::TILE;
+    const uint16_t* sV = sVbase + buf * S::TILE;
     const bool prefix = i < n_pre;
     const int key0 = prefix ? i * KT : lo + (i - n_pre) * KT;
     const int valid = prefix ? min(KT, P - key0) : min(KT, r1 - key0);
-    // whole tile in the future of every row of this wave: nothing to add
+    // a local tile entirely in the future of every row of this wave adds nothing
     const bool skip = !prefix && key0 > wrow0 + 32 * RB - 1;
     if (!skip) {
-      f32x16 s[RB][KT / 32];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int n = 0; n < KT / 32; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[rb][n][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-#pragma unroll
-        for (int n = 0; n < KT / 32; ++n) {
-          const bf16x8 a = as_bf16x8(load16(sK + (n * 32 + l32) * Tile<D>::KSTR + ks * 16 + half * 8));
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) s[rb][n] = mfma32(a, qf[rb][ks], s[rb][n]);
-        }
-      }
-
       const bool need_mask = prefix ? (valid < KT) : (key0 + KT - 1 > wrow0);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (need_mask) {
-          const int row = wrow0 + rb * 32 + l32;
-#pragma unroll
-          for (int n = 0; n < KT / 32; ++n)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kk = n * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-              const bool dead = prefix ? (kk >= valid) : (key0 + kk > row);
-              if (dead) s[rb][n][r] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int n = 0; n < KT / 32; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][n][r]);
-        mx = fmaxf(mx, swap_half(mx));
-        const float mxs = mx * p.scale_log2;
-        if (mxs > m_run[rb] + kLazyTau) {
-          const float alpha = fast_exp2(m_run[rb] - mxs);
-          m_run[rb] = mxs;
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
-        }
-        const float mu = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-        float ls = 0.f;
-#pragma unroll
-        for (int n = 0; n < KT / 32; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(fmaf(s[rb][n][r], p.scale_log2, -mu));
-            ls += e;
-            s[rb][n][r] = e;
-          }
-        l_run[rb] += ls;
-      }
-
-      // O^T += V^T . P^T, 16 keys per MFMA
-#pragma unroll
-      for (int c = 0; c < KT / 16; ++c) {
-        bf16x8 pf[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const f32x16& sv = s[rb][c / 2];
-          const int b0 = (c % 2) * 8;
-          u32x4 w = {pack_bf16x2(sv[b0 + 0], sv[b0 + 1]), pack_bf16x2(sv[b0 + 2], sv[b0 + 3]),
-                     pack_bf16x2(sv[b0 + 4], sv[b0 + 5]), pack_bf16x2(sv[b0 + 6], sv[b0 + 7])};
-          pf[rb] = as_bf16x8(w);
-        }
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const bf16x8 a = as_bf16x8(load16(sV + (db * 32 + l32) * Tile<D>::VSTR + c * 16 + half * 8));
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(a, pf[rb], o[rb][db]);
-        }
-      }
+      if (need_mask)
+        attend_tile<D, RB, KT, true>(sK, sV, qf, o, m_run, l_run, p.scale_log2, prefix, key0,
+                                     valid, wrow0);
+      else
+        attend_tile<D, RB, KT, false>(sK, sV, qf, o, m_run, l_run, p.scale_log2, prefix, key0,
+                                      valid, wrow0);
     }
-
-    if (i + 1 < ntiles) stage_store<D>(st, sKbase + (buf ^ 1) * KSZ, sVbase + (buf ^ 1) * VSZ);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -300,10 +312,10 @@ __device__ void process_tile(const AttnParams& p, int h, int g, int v, int t, ui
   }
 }
 
-template <int D, int RB>
-__global__ __launch_bounds__(kThreads) void attn_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * KT * Tile<D>::KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * D * Tile<D>::VSTR];
+template <int D, int NW, int RB, int KT>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2 * Shape<D, NW, RB, KT>::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2 * Shape<D, NW, RB, KT>::TILE];
   const uint32_t total = (uint32_t)p.n_units * (uint32_t)p.hq;
   const uint32_t L = xcd_contiguous(blockIdx.x, total);
   const int unit = p.unit_begin + (int)(L / p.hq);
@@ -311,27 +323,64 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnParams p) {
   const int g = h / p.group;
   int va, ta, vb, tb;
   p.sched.decode(unit, va, ta, vb, tb);
-  if (va >= 0) process_tile<D, RB>(p, h, g, va, ta, sK, sV);
-  if (vb >= 0) process_tile<D, RB>(p, h, g, vb, tb, sK, sV);
+  // one code path for both parts of a unit (keeps the kernel small for the instruction cache)
+  for (int part = 0; part < 2; ++part) {
+    const int v = part == 0 ? va : vb;
+    const int t = part == 0 ? ta : tb;
+    if (v >= 0) process_tile<D, NW, RB, KT>(p, h, g, v, t, sK, sV);
+  }
 }
 
-constexpr int kRB = 1;
+// Kernel variant: NW waves per workgroup, 32*RB rows per wave, KT keys per tile.
+// APBV_ATTN_CFG = "NWxRBxKT" (e.g. "8x1x64") overrides the default for tuning runs.
+struct Cfg {
+  int nw, rb, kt;
+};
+Cfg config() {
+  static const Cfg c = [] {
+    const Cfg def = {8, 1, 64};
+    const char* e = getenv("APBV_ATTN_CFG");
+    if (e == nullptr) return def;
+    const Cfg known[] = {{4, 2, 64}, {4, 2, 32}, {4, 1, 64}, {8, 1, 64}, {8, 1, 32}};
+    for (const Cfg& k : known) {
+      char buf[16];
+      snprintf(buf, sizeof(buf), "%dx%dx%d", k.nw, k.rb, k.kt);
+      if (strcmp(buf, e) == 0) return k;
+    }
+    return def;
+  }();
+  return c;
+}
+
+template <int D, int NW, int RB, int KT>
+void launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_kernel<D, NW, RB, KT>), grid, dim3(NW * 64), 0, stream, p);
+}
+
+template <int D>
+hipError_t launch_d(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  const Cfg c = config();
+  if (c.nw == 4 && c.rb == 2 && c.kt == 64) launch_one<D, 4, 2, 64>(p, grid, stream);
+  else if (c.nw == 4 && c.rb == 2) launch_one<D, 4, 2, 32>(p, grid, stream);
+  else if (c.nw == 4) launch_one<D, 4, 1, 64>(p, grid, stream);
+  else if (c.kt == 32) launch_one<D, 8, 1, 32>(p, grid, stream);
+  else launch_one<D, 8, 1, 64>(p, grid, stream);
+  return hipGetLastError();
+}
 
 }  // namespace
 
 int attn_tile_rows(int head_dim) {
-  return (head_dim == 64 || head_dim == 128) ? kWaves * 32 * kRB : 0;
+  const Cfg c = config();
+  return (head_dim == 64 || head_dim == 128) ? c.nw * 32 * c.rb : 0;
 }
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream) {
   const uint64_t total = (uint64_t)p.n_units * (uint64_t)p.hq;
   if (total == 0) return hipSuccess;
-  dim3 grid((uint32_t)total), block(kThreads);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((attn_kernel<128, kRB>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_kernel<64, kRB>), grid, block, 0, stream, p);
-  return hipGetLastError();
+  if (p.sched.tile_rows != attn_tile_rows(head_dim)) return hipErrorInvalidValue;
+  const dim3 grid((uint32_t)total);
+  return head_dim == 128 ? launch_d<128>(p, grid, stream) : launch_d<64>(p, grid, stream);
 }
 
 }  // namespace apbv
