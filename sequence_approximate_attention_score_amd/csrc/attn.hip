@@ -17,9 +17,10 @@
 //    operand comes straight from a row-major V tile through ds_read_b64_tr_b16 (two
 //    transposing 8-byte reads per operand), so the rescale factor of a row is lane-local.
 //  * K and V tiles of 64 keys go global -> LDS with global_load_lds_dwordx4 (no register
-//    staging), XOR-swizzled per row so that both read patterns are bank-conflict free;
-//    double-buffered, the next tile's loads in flight while the current one is computed,
-//    one barrier per tile.
+//    staging) into padded rows (K: +16 B, V: +32 B), which keeps the 128-bit operand reads
+//    and the transposing reads near the LDS peak while every LDS read address is a per-lane
+//    base plus a compile-time offset; double-buffered, the next tile's loads in flight
+//    while the current one is computed, one barrier per tile.
 //  * Online softmax in log2 units with a lazy rescale: the running offset is only raised
 //    when a tile's maximum exceeds it by more than 8 (probabilities stay <= 256), which is
 //    exact up to rounding and skips almost every O rescale. Masking code runs only on
@@ -40,27 +41,31 @@ namespace {
 constexpr float kLazyTau = 8.0f;   // log2 headroom before the running offset is raised
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Shape of one kernel variant: NW waves, 32*RB query rows per wave, KT keys per tile.
+// Shape of one kernel variant: NW waves, 32*RB query rows per wave, KT = 64 keys per tile.
+// One LDS stage holds the K tile (rows padded to D+8 elements) followed by the V tile
+// (rows padded to D+16 elements). Both are filled by global->LDS loads of 1 KB per wave
+// (64 lanes x 16 B); the padding keeps the MFMA operand reads bank-conflict free while
+// every LDS read is a per-lane base plus a compile-time offset.
 template <int D, int NW, int RB, int KT>
 struct Shape {
-  static constexpr int kThreads = NW * 64;
+  static_assert(KT == 64, "the padded tile layout assumes 64-key tiles");
   static constexpr int M = NW * 32 * RB;           // query rows per tile
-  static constexpr int TILE = KT * D;              // elements per K (or V) tile buffer
-  static constexpr int SEG = TILE * 2 / 1024;      // 1 KB wave-load segments per buffer
-  static constexpr int LOADS = 2 * SEG / NW;       // direct loads per lane per tile (K + V)
-  static_assert((2 * SEG) % NW == 0, "tile must split evenly over the waves");
+  static constexpr int KSTR = D + 8;               // K row stride (elements)
+  static constexpr int VSTR = D + 16;              // V row stride (elements)
+  static constexpr int KSLOT = KSTR / 8;           // 16-byte slots per K row
+  static constexpr int VSLOT = VSTR / 8;
+  static constexpr int SEGK = KT * KSLOT / 64;     // 1 KB segments of the K tile
+  static constexpr int SEGV = KT * VSLOT / 64;
+  static constexpr int SEG = SEGK + SEGV;
+  static constexpr int LOADS = (SEG + NW - 1) / NW;  // load slots per lane per tile
+  static constexpr int STAGE = SEG * 512;          // elements per LDS stage
+  static constexpr int VOFF = SEGK * 512;          // V tile offset inside a stage
 };
 
-// LDS layouts (both tiles row-major, KT rows of D bf16, no padding, filled 1 KB per
-// wave-load by global->LDS loads; the 16-byte chunk c of row r sits at position c ^ f(r)):
-//  K: f(r) = r & 7       -> the MFMA A-operand read (8 rows, one chunk) touches 8 chunks.
-//  V: f(r) = 2 * (r & 3) -> the transposing read (4 rows x 2 chunks per 16 lanes) touches 8.
-__device__ __forceinline__ int swz_k(int r) { return r & 7; }
-__device__ __forceinline__ int swz_v(int r) { return 2 * (r & 3); }
-
-// Source of one key tile: base row pointer for K and V, row stride, valid rows (>= 1).
+// Source of one key tile: K and V of its first row, row stride, valid rows (>= 1).
 struct KeySrc {
   const uint16_t* k;
   const uint16_t* v;
@@ -68,47 +73,65 @@ struct KeySrc {
   int valid;
 };
 
-// K and V tile -> LDS, no registers involved. Rows past `valid` repeat the last valid row;
-// those keys are masked in the scores, so their values only need to be finite.
+// Per-lane (row, column) of each load slot; padding slots repeat column 0 of their row.
 template <int D, int NW, int RB, int KT>
-__device__ __forceinline__ void load_tile(uint16_t* sK, uint16_t* sV, const KeySrc& src) {
+struct LoadMap {
+  int row[Shape<D, NW, RB, KT>::LOADS];
+  int col[Shape<D, NW, RB, KT>::LOADS];
+  __device__ __forceinline__ void init() {
+    using S = Shape<D, NW, RB, KT>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < S::LOADS; ++j) {
+      const int seg = j * NW + wave;
+      const bool is_v = seg >= S::SEGK;
+      const int slots = is_v ? S::VSLOT : S::KSLOT;
+      const int q = (is_v ? seg - S::SEGK : seg) * 64 + lane;
+      const int c = q % slots;
+      row[j] = min(q / slots, KT - 1);
+      col[j] = c < D / 8 ? c * 8 : 0;
+    }
+  }
+};
+
+// K and V tile -> one LDS stage, no registers involved. Rows past `valid` repeat the last
+// valid row; those keys are masked in the scores, so their values only need to be finite.
+template <int D, int NW, int RB, int KT>
+__device__ __forceinline__ void load_tile(uint16_t* stage, const LoadMap<D, NW, RB, KT>& lm,
+                                          const KeySrc& src) {
   using S = Shape<D, NW, RB, KT>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < S::LOADS; ++j) {
-    const int seg = j * NW + wave;                       // 0 .. 2*SEG-1 (K first, then V)
-    const bool is_v = seg >= S::SEG;
-    const int sg = is_v ? seg - S::SEG : seg;
-    const int e = sg * 512 + lane * 8;                   // element this lane fills
-    const int r = e / D, pos = (e % D) / 8;
-    const int c = pos ^ (is_v ? swz_v(r) : swz_k(r));    // logical chunk stored at `pos`
-    const int rr = min(r, src.valid - 1);
-    const uint16_t* g = (is_v ? src.v : src.k) + rr * src.stride + c * 8;
-    __builtin_amdgcn_global_load_lds(g, (is_v ? sV : sK) + sg * 512, 16, 0, 0);
+    const int seg = j * NW + wave;
+    if (seg < S::SEG) {
+      const bool is_v = seg >= S::SEGK;
+      const int off = min(lm.row[j], src.valid - 1) * (int)src.stride + lm.col[j];
+      __builtin_amdgcn_global_load_lds((is_v ? src.v : src.k) + off, stage + seg * 512, 16, 0, 0);
+    }
   }
 }
 
 // One key tile for one wave: S^T = K.Q^T, (masked) online softmax, O^T += V^T.P^T.
-template <int D, int RB, int KT, bool MASK>
-__device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* sV,
-                                            const bf16x8 (&qf)[RB][D / 16],
+template <int D, int NW, int RB, int KT, bool MASK>
+__device__ __forceinline__ void attend_tile(const uint16_t* stage, const bf16x8 (&qf)[RB][D / 16],
                                             f32x16 (&o)[RB][D / 32], float (&m_run)[RB],
                                             float (&l_run)[RB], float scale_log2, bool prefix,
                                             int key0, int valid, int wrow0) {
+  using S = Shape<D, NW, RB, KT>;
   constexpr int ND = D / 32, NK = D / 16, NN = KT / 32;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const f32x16 zero = {};
 
   // S^T[key, row] for NN blocks of 32 keys; A = K rows from LDS, B = Q^T from registers
+  const uint16_t* kbase = stage + l32 * S::KSTR + half * 8;
   f32x16 s[RB][NN];
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) {
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
-      const int row = n * 32 + l32;
-      const int pos = (2 * ks + half) ^ swz_k(row);
-      const bf16x8 a = as_bf16x8(load16(sK + row * D + pos * 8));
+      const bf16x8 a = as_bf16x8(load16(kbase + n * 32 * S::KSTR + ks * 16));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         s[rb][n] = mfma32(a, qf[rb][ks], ks == 0 ? zero : s[rb][n]);
@@ -164,6 +187,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* 
   // transposing reads: source lane j of each 16-lane group points at key row
   // 16c + 8t + 4h + j/4 and d columns 32db + 16*(group % 2) + 4*(j % 4) .. +3.
   const int grp = (lane >> 4) & 1, j16 = lane & 15;
+  const uint16_t* vbase = stage + S::VOFF + (4 * half + (j16 >> 2)) * S::VSTR + 16 * grp + 4 * (j16 & 3);
 #pragma unroll
   for (int c = 0; c < KT / 16; ++c) {
     bf16x8 pf[RB];
@@ -177,18 +201,11 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* 
     }
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
-      s16x4 part[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = 16 * c + 8 * t + 4 * half + (j16 >> 2);
-        const int d0 = 32 * db + 16 * grp + 4 * (j16 & 3);
-        const int pos = (d0 >> 3) ^ swz_v(row);
-        const uint16_t* src = sV + row * D + pos * 8 + (d0 & 7);
-        part[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-      }
+      const uint16_t* src = vbase + 16 * c * S::VSTR + 32 * db;
+      const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+      const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * S::VSTR));
       typedef short s16x8 __attribute__((ext_vector_type(8)));
-      const s16x8 both = {part[0][0], part[0][1], part[0][2], part[0][3],
-                          part[1][0], part[1][1], part[1][2], part[1][3]};
+      const s16x8 both = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       const bf16x8 va = __builtin_bit_cast(bf16x8, both);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(va, pf[rb], o[rb][db]);
@@ -198,7 +215,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* 
 
 template <int D, int NW, int RB, int KT>
 __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, int v, int t,
-                                             uint16_t* sKbase, uint16_t* sVbase) {
+                                             uint16_t* lds, const LoadMap<D, NW, RB, KT>& lm) {
   using S = Shape<D, NW, RB, KT>;
   constexpr int M = S::M;
   constexpr int ND = D / 32;     // 32-wide d blocks of O^T
@@ -259,17 +276,14 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, 
     return s;
   };
 
-  load_tile<D, NW, RB, KT>(sKbase, sVbase, source(0));
+  load_tile<D, NW, RB, KT>(lds, lm, source(0));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int i = 0; i < ntiles; ++i) {
     const int buf = i & 1;
-    if (i + 1 < ntiles)
-      load_tile<D, NW, RB, KT>(sKbase + (buf ^ 1) * S::TILE, sVbase + (buf ^ 1) * S::TILE,
-                               source(i + 1));
-    const uint16_t* sK = sKbase + buf * S::TILE;
-    const uint16_t* sV = sVbase + buf * S::TILE;
+    if (i + 1 < ntiles) load_tile<D, NW, RB, KT>(lds + (buf ^ 1) * S::STAGE, lm, source(i + 1));
+    const uint16_t* stage = lds + buf * S::STAGE;
     const bool prefix = i < n_pre;
     const int key0 = prefix ? i * KT : lo + (i - n_pre) * KT;
     const int valid = prefix ? min(KT, P - key0) : min(KT, r1 - key0);
@@ -278,11 +292,11 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, 
     if (!skip) {
       const bool need_mask = prefix ? (valid < KT) : (key0 + KT - 1 > wrow0);
       if (need_mask)
-        attend_tile<D, RB, KT, true>(sK, sV, qf, o, m_run, l_run, p.scale_log2, prefix, key0,
-                                     valid, wrow0);
+        attend_tile<D, NW, RB, KT, true>(stage, qf, o, m_run, l_run, p.scale_log2, prefix, key0,
+                                         valid, wrow0);
       else
-        attend_tile<D, RB, KT, false>(sK, sV, qf, o, m_run, l_run, p.scale_log2, prefix, key0,
-                                      valid, wrow0);
+        attend_tile<D, NW, RB, KT, false>(stage, qf, o, m_run, l_run, p.scale_log2, prefix, key0,
+                                          valid, wrow0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -314,8 +328,9 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, 
 
 template <int D, int NW, int RB, int KT>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[2 * Shape<D, NW, RB, KT>::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[2 * Shape<D, NW, RB, KT>::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * Shape<D, NW, RB, KT>::STAGE];
+  LoadMap<D, NW, RB, KT> lm;
+  lm.init();
   const uint32_t total = (uint32_t)p.n_units * (uint32_t)p.hq;
   const uint32_t L = xcd_contiguous(blockIdx.x, total);
   const int unit = p.unit_begin + (int)(L / p.hq);
@@ -327,12 +342,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   for (int part = 0; part < 2; ++part) {
     const int v = part == 0 ? va : vb;
     const int t = part == 0 ? ta : tb;
-    if (v >= 0) process_tile<D, NW, RB, KT>(p, h, g, v, t, sK, sV);
+    if (v >= 0) process_tile<D, NW, RB, KT>(p, h, g, v, t, lds, lm);
   }
 }
 
 // Kernel variant: NW waves per workgroup, 32*RB rows per wave, KT keys per tile.
-// APBV_ATTN_CFG = "NWxRBxKT" (e.g. "8x1x64") overrides the default for tuning runs.
+// APBV_ATTN_CFG = "NWxRBxKT" ("8x1x64", "4x1x64", "4x2x64") overrides the default for
+// tuning runs.
 struct Cfg {
   int nw, rb, kt;
 };
@@ -341,7 +357,7 @@ Cfg config() {
     const Cfg def = {8, 1, 64};
     const char* e = getenv("APBV_ATTN_CFG");
     if (e == nullptr) return def;
-    const Cfg known[] = {{4, 2, 64}, {4, 2, 32}, {4, 1, 64}, {8, 1, 64}, {8, 1, 32}};
+    const Cfg known[] = {{4, 2, 64}, {4, 1, 64}, {8, 1, 64}};
     for (const Cfg& k : known) {
       char buf[16];
       snprintf(buf, sizeof(buf), "%dx%dx%d", k.nw, k.rb, k.kt);
@@ -360,10 +376,8 @@ void launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
 template <int D>
 hipError_t launch_d(const AttnParams& p, dim3 grid, hipStream_t stream) {
   const Cfg c = config();
-  if (c.nw == 4 && c.rb == 2 && c.kt == 64) launch_one<D, 4, 2, 64>(p, grid, stream);
-  else if (c.nw == 4 && c.rb == 2) launch_one<D, 4, 2, 32>(p, grid, stream);
+  if (c.nw == 4 && c.rb == 2) launch_one<D, 4, 2, 64>(p, grid, stream);
   else if (c.nw == 4) launch_one<D, 4, 1, 64>(p, grid, stream);
-  else if (c.kt == 32) launch_one<D, 8, 1, 32>(p, grid, stream);
   else launch_one<D, 8, 1, 64>(p, grid, stream);
   return hipGetLastError();
 }
