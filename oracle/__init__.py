@@ -5,7 +5,9 @@ TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` an
 """
 from . import apbv_oracle
 from .apbv_oracle import (ambiguous_positions, approx_attention_prefill, attend, gather_prefix,
-                          kv_head, passing_scores, select_passing)
+                          kv_head, merge_partials, passing_scores, query_attention,
+                          select_passing)
 
 __all__ = ["apbv_oracle", "ambiguous_positions", "approx_attention_prefill", "attend",
-           "gather_prefix", "kv_head", "passing_scores", "select_passing"]
+           "gather_prefix", "kv_head", "merge_partials", "passing_scores", "query_attention",
+           "select_passing"]

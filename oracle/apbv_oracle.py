@@ -13,8 +13,10 @@ Sources (the method is described only in prose; no formula or listing is printed
   query-to-context attention scores and collects them as passing blocks, and computes
   attention over anchor, local context and the collected passing blocks.
 * Same page, part 2 "Ottimizzazioni a Livello di Sistema": ZigZag pairing of virtual hosts
-  h and 2H-1-h balances the passing-block length per physical host; the fused query forward
-  merges partial results through the log-sum-exp that FlashAttention returns.
+  h and 2H-1-h balances the passing-block length per physical host; the fused forward of
+  context and query ("Forward Fuso di Contesto e Query") runs the query block's rows with
+  the context and merges their partial results over different key sets through the
+  log-sum-exp that flash attention returns.
 * Same page, "Limitazioni": with a single block the method is plain (flash) attention.
 
 Readings taken where the pages are silent (each one is listed with its reason in the design
@@ -29,7 +31,9 @@ notes of the repository):
   sequence order, each in ascending position order;
 * selection keeps the l_p largest scores of a block, ties to the lower position, decided on
   the float32-rounded scores (the precision of the GPU kernel's scores);
-* mask: anchor and passing keys fully visible, local keys causal (j <= i).
+* mask: anchor and passing keys fully visible, local keys causal (j <= i);
+* the query block's rows are exact: they see the anchor, all N context keys and the query
+  block's keys up to their own position.
 
 Parity pins are in ``tests/test_oracle.py``; none of the pages prints a worked example,
 so agreement with the paper's own outputs is unpinned.
@@ -177,6 +181,57 @@ def approx_attention_prefill(q_query, q_ctx, k_ctx, v_ctx, k_anchor, v_anchor, b
                       hq, hkv, scale, rows=rows, heads=heads)
     return {"scores": s, "scores32": s32, "sel": sel, "k_pre": k_pre, "v_pre": v_pre,
             "out": out, "lse": lse}
+
+
+# --------------------------------------------------------------------------------------
+# Step 5 - rows of the query block (fused query forward).
+# --------------------------------------------------------------------------------------
+def query_attention(q_query, k_query, v_query, k_anchor, v_anchor, k_ctx, v_ctx, hq: int,
+                    hkv: int, scale: float, heads=None):
+    """Attention of the query block's rows; returns (out ``[l_q, hq, d]``, lse ``[hq, l_q]``).
+
+    The query block closes the sequence [anchor | context | query block] and its rows are
+    not approximated: row i of head h sees every anchor key, every context key and the query
+    block's keys 0..i. ``k_query`` may hold fewer rows than ``q_query`` (query key j is
+    visible to query row i iff j <= i). Entries of heads outside ``heads`` are NaN.
+    """
+    q = _as64(q_query)
+    l_q, d = q.shape[0], q.shape[2]
+    n_q = np.asarray(k_query).shape[0]
+    out = np.full((l_q, hq, d), np.nan)
+    lse = np.full((hq, l_q), np.nan)
+    rows = np.arange(l_q)
+    for h in (range(hq) if heads is None else heads):
+        g = kv_head(h, hq, hkv)
+        keys = np.concatenate([_as64(k_anchor[:, g]), _as64(k_ctx[:, g]), _as64(k_query[:, g])])
+        vals = np.concatenate([_as64(v_anchor[:, g]), _as64(v_ctx[:, g]), _as64(v_query[:, g])])
+        n_before = keys.shape[0] - n_q
+        z = scale * (q[:, h, :] @ keys.T)                         # [l_q, l_a + N + n_q]
+        z[:, n_before:][np.arange(n_q)[None, :] > rows[:, None]] = -np.inf
+        m = np.max(z, axis=1, keepdims=True)
+        e = np.exp(z - m)
+        l = np.sum(e, axis=1, keepdims=True)
+        out[:, h, :] = (e @ vals) / l
+        lse[h, :] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def merge_partials(outs, lses):
+    """Attention over a union of disjoint key sets from the attention over each set
+    (the fused forward's merge of partial query results through their log-sum-exp).
+
+    ``outs[s]`` ``[rows, heads, d]`` and ``lses[s]`` ``[heads, rows]`` are the normalised
+    output and natural-log lse of part s; a part in which a row sees no key has lse -inf and
+    contributes nothing. Returns (out, lse) of the union.
+    """
+    L = np.stack([_as64(x) for x in lses])                         # [S, heads, rows]
+    top = np.max(L, axis=0)
+    w = np.exp(L - top[None])                                      # weight of each part
+    total = np.sum(w, axis=0)
+    lse = top + np.log(total)
+    wt = np.transpose(w / total[None], (0, 2, 1))[..., None]      # [S, rows, heads, 1]
+    o = np.stack([np.nan_to_num(_as64(x)) for x in outs])
+    return np.sum(wt * o, axis=0), lse
 
 
 # --------------------------------------------------------------------------------------

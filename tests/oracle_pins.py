@@ -270,7 +270,71 @@ def pin_hand_worked_golden(orc):
             assert np.allclose(r["scores"][0], exp_s, atol=1e-15)
 
 
+def query_problem(seed, **kw):
+    p = tiny_problem(seed, **kw)
+    rng = np.random.default_rng(seed + 1000)
+    l_q, hkv, d = p["q_query"].shape[0], p["hkv"], p["q_query"].shape[2]
+    p["k_query"] = rng.standard_normal((l_q, hkv, d))
+    p["v_query"] = rng.standard_normal((l_q, hkv, d))
+    return p
+
+
+def run_query(orc, p, **over):
+    a = dict(p, **over)
+    return orc.query_attention(a["q_query"], a["k_query"], a["v_query"], a["k_anchor"],
+                               a["v_anchor"], a["k_ctx"], a["v_ctx"], a["hq"], a["hkv"],
+                               a["scale"])
+
+
+def pin_query_rows_are_dense_causal_tail(orc):
+    """The query block closes the sequence: its rows equal the last l_q rows of dense causal
+    attention (torch SDPA) over [anchor | context | query block]; lse equals the
+    log-sum-exp (scipy) of each row's visible logits, enumerated one key at a time."""
+    from scipy.special import logsumexp
+    p = query_problem(11)
+    out, lse = run_query(orc, p)
+    rng = np.random.default_rng(12)
+    l_q, hq, d = p["q_query"].shape
+    G = hq // p["hkv"]
+    for h in range(hq):
+        g = h // G
+        K = np.concatenate([p["k_anchor"][:, g], p["k_ctx"][:, g], p["k_query"][:, g]])
+        V = np.concatenate([p["v_anchor"][:, g], p["v_ctx"][:, g], p["v_query"][:, g]])
+        Q = np.concatenate([rng.standard_normal((K.shape[0] - l_q, d)), p["q_query"][:, h]])
+        ref = sdpa(Q, K, V, p["scale"], causal=True)[-l_q:]
+        assert np.allclose(out[:, h], ref, atol=1e-12, rtol=0), "query rows vs dense causal"
+        for i in range(l_q):
+            visible = [p["scale"] * float(K[j] @ p["q_query"][i, h])
+                       for j in range(K.shape[0] - l_q + i + 1)]
+            assert math.isclose(lse[h, i], logsumexp(visible), rel_tol=0, abs_tol=1e-12)
+
+
+def pin_query_merge_of_split_keys(orc):
+    """Attention over a union of key sets is recovered from the parts through their lse:
+    context split at a random row into [anchor | ctx[:m] | query] and [ctx[m:]]; a part in
+    which no key is visible (lse -inf, output NaN) changes nothing; V = const gives const."""
+    p = query_problem(13)
+    whole_o, whole_l = run_query(orc, p)
+    N = p["k_ctx"].shape[0]
+    for m in (1, 7, N - 1):
+        a_o, a_l = run_query(orc, p, k_ctx=p["k_ctx"][:m], v_ctx=p["v_ctx"][:m])
+        b_o, b_l = run_query(orc, p, k_ctx=p["k_ctx"][m:], v_ctx=p["v_ctx"][m:],
+                             k_anchor=p["k_anchor"][:0], v_anchor=p["v_anchor"][:0],
+                             k_query=p["k_query"][:0], v_query=p["v_query"][:0])
+        o, l = orc.merge_partials([a_o, b_o], [a_l, b_l])
+        assert np.allclose(o, whole_o, atol=1e-12, rtol=0) and np.allclose(l, whole_l, atol=1e-12)
+    empty_o = np.full_like(whole_o, np.nan)
+    empty_l = np.full_like(whole_l, -np.inf)
+    o, l = orc.merge_partials([whole_o, empty_o], [whole_l, empty_l])
+    assert np.allclose(o, whole_o, atol=1e-14) and np.allclose(l, whole_l, atol=1e-14)
+    c = np.full_like(p["v_ctx"], 0.75)
+    o, _ = run_query(orc, p, v_ctx=c, v_anchor=np.full_like(p["v_anchor"], 0.75),
+                     v_query=np.full_like(p["v_query"], 0.75))
+    assert np.allclose(o, 0.75, atol=1e-14, rtol=0)
+
+
 PINS = [pin_bruteforce_mask, pin_single_block_is_dense_causal, pin_full_passing_is_dense_causal,
         pin_probability_mass, pin_scores_are_library_softmax_sums, pin_score_query_permutation,
         pin_needles_rank_first, pin_selection_definition, pin_no_passing_is_anchor_plus_local,
-        pin_hand_worked_golden]
+        pin_hand_worked_golden, pin_query_rows_are_dense_causal_tail,
+        pin_query_merge_of_split_keys]

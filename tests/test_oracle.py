@@ -55,6 +55,18 @@ MUTATIONS = {
         ("return e / np.sum(e, axis=-1, keepdims=True)", "return e"),
     "selection indices relative to the block":
         ("sel[v, g] = np.sort(order[:l_pass]) + lo", "sel[v, g] = np.sort(order[:l_pass])"),
+    "query rows see the next query key":
+        ("np.arange(n_q)[None, :] > rows[:, None]] = -np.inf",
+         "np.arange(n_q)[None, :] > rows[:, None] + 1] = -np.inf"),
+    "query rows ignore the anchor keys":
+        ("keys = np.concatenate([_as64(k_anchor[:, g]),", "keys = np.concatenate([0 * _as64(k_anchor[:, g]),"),
+    "query rows use the interleaved KV head":
+        ("g = kv_head(h, hq, hkv)\n        keys = np.concatenate([_as64(k_anchor",
+         "g = h % hkv\n        keys = np.concatenate([_as64(k_anchor"),
+    "merge weights not normalised":
+        ("wt = np.transpose(w / total[None], (0, 2, 1))", "wt = np.transpose(w, (0, 2, 1))"),
+    "merged lse without the log":
+        ("lse = top + np.log(total)", "lse = top + total"),
 }
 
 
