@@ -4,6 +4,8 @@ One step = one layer of the hot path on the 128K-token Qwen2.5-VL-7B-shaped work
 (28 query / 4 KV heads, head_dim 128, 16 virtual blocks of 8K on 8 ZigZag buckets,
 anchor 2048, query block 128, l_p 1024): score_select -> gather_passing ->
 approx_attn_prefill, with every input already resident in HBM. Prints one JSON line.
+Beside the timed steps it also times the query block's rows (query_forward), each ZigZag
+bucket's attention alone, and the attention with the last-level cache flushed.
 
     python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
                     [--profile] [--calib-copy]
@@ -29,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "approx-attn prefill tokens/s per layer at 128K ctx; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 ATTN_SOURCES = ["sequence_approximate_attention_score_amd/csrc/attn.hip",
+                "sequence_approximate_attention_score_amd/csrc/attn_core.h",
                 "sequence_approximate_attention_score_amd/csrc/apbv_device.h",
                 "sequence_approximate_attention_score_amd/csrc/apbv_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_c2_traffic.txt")
@@ -42,6 +45,28 @@ def attention_flops(block_starts, l_anchor, l_pass, hq, d) -> float:
         P = l_anchor + v * l_pass
         pairs += L * P + L * (L + 1) // 2
     return float(pairs) * hq * 4 * d
+
+
+def gather_bytes(lay, d) -> float:
+    """Algorithmic bytes of the gather: K and V prefix rows read once and written once."""
+    return 2.0 * 2.0 * lay.hkv * lay.pre_rows * d * 2
+
+
+def median_ms(fn, reps: int, before=None) -> float:
+    """Median duration (HIP events on the current stream) of ``fn`` over ``reps`` calls;
+    ``before`` runs ahead of each call, outside its events."""
+    import torch
+    times = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return float(np.median(times))
 
 
 def attn_source_sha() -> str:
@@ -149,7 +174,8 @@ def main():
     print(f"# generating {w.name}: {w.description}", file=sys.stderr, flush=True)
     x = generate(w)
     up = lambda n: torch.from_numpy(x.bits[n].view(np.int16)).to(dev).view(torch.bfloat16)
-    d = {n: up(n) for n in ("q_query", "q_ctx", "k_ctx", "v_ctx", "k_anchor", "v_anchor")}
+    d = {n: up(n) for n in ("q_query", "q_ctx", "k_ctx", "v_ctx", "k_anchor", "v_anchor",
+                            "k_query", "v_query")}
     lay = apbv.Layout(x.block_starts, l_anchor=w.l_anchor, l_query=w.l_query, l_pass=w.l_pass,
                       hq=w.hq, hkv=w.hkv, head_dim=w.head_dim, zigzag=True)
     ws = torch.empty(max(apbv.score_select_workspace(lay), 256), dtype=torch.uint8, device=dev)
@@ -157,7 +183,17 @@ def main():
     kp = torch.empty((w.hkv, lay.pre_rows, w.head_dim), dtype=torch.bfloat16, device=dev)
     vp = torch.empty_like(kp)
     out = torch.empty((x.N, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
+    q_ws = torch.empty(max(apbv.query_forward_workspace(lay), 256), dtype=torch.uint8, device=dev)
+    q_out = torch.empty((w.l_query, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
+
+    def attention(rb=0, re=0):
+        apbv.approx_attn_prefill(lay, d["q_ctx"], kp, vp, d["k_ctx"], d["v_ctx"], out=out,
+                                 range_begin=rb, range_end=re)
+
+    def query_rows():
+        apbv.query_forward(lay, d["q_query"], d["k_query"], d["v_query"], d["k_anchor"],
+                           d["v_anchor"], d["k_ctx"], d["v_ctx"], out=q_out, workspace=q_ws)
 
     def step(ev=None):
         if ev is not None:
@@ -169,7 +205,7 @@ def main():
                             k_pre=kp, v_pre=vp)
         if ev is not None:
             ev[2].record()
-        apbv.approx_attn_prefill(lay, d["q_ctx"], kp, vp, d["k_ctx"], d["v_ctx"], out=out)
+        attention()
         if ev is not None:
             ev[3].record()
 
@@ -187,6 +223,17 @@ def main():
     per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                     for e in evs])   # ms: score_select, gather, attention
     ms_step = (t1 - t0) * 1e3 / steps
+    # beside the timed steps: the query block's rows, each ZigZag bucket alone, and the
+    # attention with the 256 MB last-level cache flushed by a 512 MiB write before each call
+    # (a profiled run keeps every attention launch whole, so its kernel statistics match)
+    q_ms = median_ms(query_rows, 2 if args.profile else 5)
+    bucket_ms, cold_ms = None, None
+    if not args.profile:
+        bucket_ms = [median_ms(lambda b=b: attention(b, b + 1), 3)
+                     for b in range(apbv.num_buckets(lay))]
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ms = median_ms(attention, 5, before=lambda: flush.fill_(1))
+        del flush
     if args.calib_copy:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
         b = torch.empty_like(a)
@@ -222,6 +269,14 @@ def main():
         "breakdown_ms": {"score_select": float(per[:, 0].mean()), "gather": float(per[:, 1].mean()),
                          "attention": attn_ms},
         "attention_only_tokens_per_s": x.N / (attn_ms * 1e-3),
+        "attention_ms_median_warm": float(np.median(per[:, 2])),
+        "attention_ms_median_cold": cold_ms,
+        "per_bucket_attention_ms": bucket_ms,
+        "bucket_max_over_mean": (max(bucket_ms) / (sum(bucket_ms) / len(bucket_ms))
+                                 if bucket_ms else None),
+        "query_forward_ms": q_ms,
+        "layer_with_query_rows_tokens_per_s": (x.N + w.l_query) / ((ms_step + q_ms) * 1e-3),
+        "gather_GBps": gather_bytes(lay, w.head_dim) / (float(per[:, 1].mean()) * 1e-3) / 1e9,
         "cpu_baseline": None,
     }
     if not (args.profile or args.no_cpu_baseline):

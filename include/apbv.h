@@ -11,6 +11,8 @@
  *      (apbv_gather_passing),
  *   3. runs attention of the block's rows over [anchor | passing blocks of the preceding
  *      blocks | the block's own keys, causal]                        (apbv_approx_attn_prefill).
+ * The rows of the query block itself, which see the whole sequence, come from
+ * apbv_query_forward.
  * All virtual blocks of the method's sequence-parallel layout live on one GPU; ZigZag
  * pairing of block p with block n-1-p (same page, "Suddivisione del Contesto e
  * Disposizione ZigZag" and "Bilanciamento del Carico dell'Attenzione Approssimata") is the
@@ -134,6 +136,38 @@ apbv_status apbv_approx_attn_prefill(const apbv_layout* layout, const apbv_bf16*
                                      const apbv_bf16* k_ctx, const apbv_bf16* v_ctx,
                                      apbv_bf16* out, float* lse, int32_t range_begin,
                                      int32_t range_end, void* stream);
+
+/* Workspace bytes needed by apbv_query_forward for this layout (written to *bytes; 0 when
+ * l_query is 0). */
+apbv_status apbv_query_forward_workspace(const apbv_layout* layout, size_t* bytes);
+
+/*
+ * Rows of the query block (same page, part 2, "Forward Fuso di Contesto e Query": the
+ * query runs in the same forward as the context and its partial results over different key
+ * sets are merged through their log-sum-exp). The query block closes the sequence
+ * [anchor | context | query block], so its rows are exact: row i of head h (KV head g) sees
+ *   k_anchor[:, g]  ++  k_ctx[0 .. N-1, g]  ++  k_query[0 .. i, g]
+ *   out[i, h, :] = softmax(scale * q_query[i,h] . keys) @ values       (bf16, round-to-nearest)
+ *   lse[h, i]    = natural-log log-sum-exp of the scaled logits         (fp32, optional)
+ * computed as partial results over chunks of at most 4096 keys (bf16 MFMA, fp32 softmax),
+ * merged in a second kernel.
+ *
+ *   q_query          [l_query, hq, d] bf16, contiguous
+ *   k_query, v_query [l_query, hkv, d] bf16, contiguous
+ *   k_anchor, v_anchor [l_anchor, hkv, d] bf16, contiguous (may be NULL if l_anchor == 0)
+ *   k_ctx, v_ctx     [N, hkv, d] bf16 (kv_row_stride)
+ *   out              [l_query, hq, d] bf16 out, contiguous
+ *   lse              [hq, l_query] fp32 out, or NULL
+ *   workspace        device buffer of at least apbv_query_forward_workspace() bytes,
+ *                    256-byte aligned (partial outputs; contents need no initialisation)
+ * With l_query == 0 nothing is launched.
+ */
+apbv_status apbv_query_forward(const apbv_layout* layout, const apbv_bf16* q_query,
+                               const apbv_bf16* k_query, const apbv_bf16* v_query,
+                               const apbv_bf16* k_anchor, const apbv_bf16* v_anchor,
+                               const apbv_bf16* k_ctx, const apbv_bf16* v_ctx, apbv_bf16* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* Number of schedulable ranges: ZigZag buckets (ceil(n/2)) if zigzag, else n_blocks.
  * Returns -1 for an invalid layout. Host only. */

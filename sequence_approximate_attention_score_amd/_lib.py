@@ -18,8 +18,9 @@ APBV_OK, APBV_EINVAL, APBV_EUNSUPPORTED, APBV_EWORKSPACE, APBV_EHIP = 0, 1, 2, 3
 MAX_BLOCKS = 64
 
 EXPORTED = ["apbv_score_select_workspace", "apbv_score_select", "apbv_gather_passing",
-            "apbv_approx_attn_prefill", "apbv_num_buckets", "apbv_schedule",
-            "apbv_attn_tile_rows", "apbv_status_str", "apbv_last_error", "apbv_version"]
+            "apbv_approx_attn_prefill", "apbv_query_forward_workspace", "apbv_query_forward",
+            "apbv_num_buckets", "apbv_schedule", "apbv_attn_tile_rows", "apbv_status_str",
+            "apbv_last_error", "apbv_version"]
 
 
 class ApbvError(RuntimeError):
@@ -53,6 +54,9 @@ def lib() -> ctypes.CDLL:
             "apbv_score_select": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
             "apbv_gather_passing": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
             "apbv_approx_attn_prefill": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
+            "apbv_query_forward_workspace": (_I32, [_LP, ctypes.POINTER(_SZ)]),
+            "apbv_query_forward": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                          _SZ, _VP]),
             "apbv_num_buckets": (_I32, [_LP]),
             "apbv_schedule": (_I32, [_LP, _I32, _I32, _VP, _I32, ctypes.POINTER(_I32)]),
             "apbv_attn_tile_rows": (_I32, [_I32]),
@@ -181,6 +185,34 @@ def approx_attn_prefill(layout: Layout, q_ctx, k_pre, v_pre, k_ctx, v_ctx, *, ou
                                           _ptr(k_ctx), _ptr(v_ctx), _ptr(out), _ptr(lse),
                                           range_begin, range_end, _stream(q_ctx.device)),
            "apbv_approx_attn_prefill")
+    return out, lse
+
+
+def query_forward_workspace(layout: Layout) -> int:
+    n = _SZ(0)
+    _check(lib().apbv_query_forward_workspace(layout.ref(), ctypes.byref(n)),
+           "apbv_query_forward_workspace")
+    return n.value
+
+
+def query_forward(layout: Layout, q_query, k_query, v_query, k_anchor, v_anchor, k_ctx, v_ctx, *,
+                  out=None, lse=None, want_lse: bool = False, workspace=None):
+    """Rows of the query block over [anchor | all context | causal query]. Returns
+    (out [l_q, hq, d] bf16, lse [hq, l_q] fp32 or None)."""
+    import torch
+    dev = k_ctx.device
+    if out is None:
+        out = torch.empty((layout.l_query, layout.hq, layout.head_dim), dtype=torch.bfloat16,
+                          device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((layout.hq, layout.l_query), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(query_forward_workspace(layout), 256), dtype=torch.uint8,
+                                device=dev)
+    _check(lib().apbv_query_forward(layout.ref(), _ptr(q_query), _ptr(k_query), _ptr(v_query),
+                                    _ptr(k_anchor), _ptr(v_anchor), _ptr(k_ctx), _ptr(v_ctx),
+                                    _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                    _stream(dev)), "apbv_query_forward")
     return out, lse
 
 

@@ -80,6 +80,38 @@ struct AttnParams {
 int attn_tile_rows(int head_dim);
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream);
 
+// ---------------------------------------------------------------- query-block rows
+// Keys of the query rows = [anchor | context | query block (causal)], cut into chunks of
+// kQueryChunk keys that never straddle two sources; chunk c of the grid computes the
+// normalised partial output and lse of every query row over its keys, and the merge
+// combines the chunks of a row through their lse.
+struct QueryParams {
+  const uint16_t* qq;   // [l_q, hq, d]
+  const uint16_t* kq;   // [l_q, hkv, d]
+  const uint16_t* vq;
+  const uint16_t* ka;   // [l_a, hkv, d]
+  const uint16_t* va;
+  const uint16_t* kc;   // [N, hkv, d] with kv_stride
+  const uint16_t* vc;
+  float* part_o;        // [n_chunks, hq, l_q, d]
+  float* part_lse;      // [n_chunks, hq, l_q] (natural log, -inf when no key is visible)
+  uint16_t* out;        // [l_q, hq, d]
+  float* lse;           // [hq, l_q] or null
+  int64_t kv_stride;
+  int32_t hq, hkv, group, l_query, l_anchor, n_tokens;
+  int32_t n_anchor_chunks, n_ctx_chunks, n_query_chunks, n_chunks, row_tiles;
+  float scale_log2;
+};
+
+constexpr int kQueryChunk = 4096;   // keys per partial (a multiple of the 64-key tile)
+
+struct QueryPlan {
+  int n_anchor_chunks, n_ctx_chunks, n_query_chunks, n_chunks, row_tiles;
+  size_t o_bytes, lse_bytes;   // workspace parts, each rounded up to 256 bytes
+};
+QueryPlan plan_query(int l_anchor, int n_tokens, int l_query, int hq, int hkv, int head_dim);
+hipError_t launch_query(const QueryParams& p, int head_dim, hipStream_t stream);
+
 // ---------------------------------------------------------------- scoring + selection
 struct ScoreParams {
   const uint16_t* qq;   // [l_q, hq, d]

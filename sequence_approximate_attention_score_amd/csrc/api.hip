@@ -309,4 +309,78 @@ apbv_status apbv_approx_attn_prefill(const apbv_layout* layout, const apbv_bf16*
   return APBV_OK;
 }
 
+apbv_status apbv_query_forward_workspace(const apbv_layout* layout, size_t* bytes) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  if (bytes == nullptr) return fail(APBV_EINVAL, "bytes is NULL");
+  const QueryPlan q = plan_query(c.l_a, c.N, c.l_q, c.hq, c.hkv, c.d);
+  *bytes = c.l_q > 0 ? q.o_bytes + q.lse_bytes : 0;
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_query_forward(const apbv_layout* layout, const apbv_bf16* q_query,
+                               const apbv_bf16* k_query, const apbv_bf16* v_query,
+                               const apbv_bf16* k_anchor, const apbv_bf16* v_anchor,
+                               const apbv_bf16* k_ctx, const apbv_bf16* v_ctx, apbv_bf16* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  const bool any = c.l_q > 0;
+  APBV_TRY(check_ptr(q_query, "q_query", any));
+  APBV_TRY(check_ptr(k_query, "k_query", any));
+  APBV_TRY(check_ptr(v_query, "v_query", any));
+  APBV_TRY(check_ptr(k_anchor, "k_anchor", any && c.l_a > 0));
+  APBV_TRY(check_ptr(v_anchor, "v_anchor", any && c.l_a > 0));
+  APBV_TRY(check_ptr(k_ctx, "k_ctx", any));
+  APBV_TRY(check_ptr(v_ctx, "v_ctx", any));
+  APBV_TRY(check_ptr(out, "out", any));
+  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return fail(APBV_EINVAL, "lse is not 4-byte aligned");
+  const QueryPlan q = plan_query(c.l_a, c.N, c.l_q, c.hq, c.hkv, c.d);
+  const size_t need = any ? q.o_bytes + q.lse_bytes : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(APBV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (workspace != nullptr && ((uintptr_t)workspace & 255u) != 0)
+    return fail(APBV_EINVAL, "workspace is not 256-byte aligned");
+  if ((uint64_t)q.row_tiles * c.hkv * q.n_chunks >= (1ull << 31))
+    return fail(APBV_EUNSUPPORTED, "query grid too large");
+  if (!any) {
+    g_err[0] = 0;
+    return APBV_OK;
+  }
+
+  QueryParams p;
+  memset(&p, 0, sizeof(p));
+  p.qq = q_query;
+  p.kq = k_query;
+  p.vq = v_query;
+  p.ka = k_anchor;
+  p.va = v_anchor;
+  p.kc = k_ctx;
+  p.vc = v_ctx;
+  p.part_o = reinterpret_cast<float*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + q.o_bytes);
+  p.out = out;
+  p.lse = lse;
+  p.kv_stride = c.kv_stride;
+  p.hq = c.hq;
+  p.hkv = c.hkv;
+  p.group = c.G;
+  p.l_query = c.l_q;
+  p.l_anchor = c.l_a;
+  p.n_tokens = c.N;
+  p.n_anchor_chunks = q.n_anchor_chunks;
+  p.n_ctx_chunks = q.n_ctx_chunks;
+  p.n_query_chunks = q.n_query_chunks;
+  p.n_chunks = q.n_chunks;
+  p.row_tiles = q.row_tiles;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+  const hipError_t e = launch_query(p, c.d, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(APBV_EHIP, "query forward launch: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
 }  // extern "C"

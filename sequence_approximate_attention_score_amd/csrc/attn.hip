@@ -7,7 +7,7 @@
 // Approssimata"; with one block and no prefix this is plain causal flash attention, as the
 // page's "Limitazioni" paragraph notes).
 //
-// Design (default variant: one workgroup = 8 waves = one query tile of 256 rows of one head,
+// Design (one workgroup = 8 waves = one query tile of 256 rows of one head,
 // 32 rows per wave, two waves per SIMD so one wave's softmax overlaps the other's MFMAs):
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: the K tile (shared by the waves) is the A
 //    operand read from LDS, the wave's Q rows are the B operand held in registers. The
@@ -27,191 +27,21 @@
 //    tiles that need it (ragged prefix end, causal diagonal).
 //  * Grid = work units x heads, remapped so each XCD gets a contiguous range: the heads of
 //    one KV group and one unit run side by side on the same XCD and share K/V in its L2.
-#include <stdio.h>
-#include <stdlib.h>
-#include <string.h>
-
 #include "apbv_device.h"
 #include "apbv_internal.h"
+#include "attn_core.h"
 
 namespace apbv {
 
 namespace {
 
-constexpr float kLazyTau = 8.0f;   // log2 headroom before the running offset is raised
+using tile::attend_tile;
+using tile::KeySrc;
+using tile::load_tile;
+using tile::LoadMap;
+using tile::Shape;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Shape of one kernel variant: NW waves, 32*RB query rows per wave, KT = 64 keys per tile.
-// One LDS stage holds the K tile (rows padded to D+8 elements) followed by the V tile
-// (rows padded to D+16 elements). Both are filled by global->LDS loads of 1 KB per wave
-// (64 lanes x 16 B); the padding keeps the MFMA operand reads bank-conflict free while
-// every LDS read is a per-lane base plus a compile-time offset.
-template <int D, int NW, int RB, int KT>
-struct Shape {
-  static_assert(KT == 64, "the padded tile layout assumes 64-key tiles");
-  static constexpr int M = NW * 32 * RB;           // query rows per tile
-  static constexpr int KSTR = D + 8;               // K row stride (elements)
-  static constexpr int VSTR = D + 16;              // V row stride (elements)
-  static constexpr int KSLOT = KSTR / 8;           // 16-byte slots per K row
-  static constexpr int VSLOT = VSTR / 8;
-  static constexpr int SEGK = KT * KSLOT / 64;     // 1 KB segments of the K tile
-  static constexpr int SEGV = KT * VSLOT / 64;
-  static constexpr int SEG = SEGK + SEGV;
-  static constexpr int LOADS = (SEG + NW - 1) / NW;  // load slots per lane per tile
-  static constexpr int STAGE = SEG * 512;          // elements per LDS stage
-  static constexpr int VOFF = SEGK * 512;          // V tile offset inside a stage
-};
-
-// Source of one key tile: K and V of its first row, row stride, valid rows (>= 1).
-struct KeySrc {
-  const uint16_t* k;
-  const uint16_t* v;
-  int64_t stride;
-  int valid;
-};
-
-// Per-lane (row, column) of each load slot; padding slots repeat column 0 of their row.
-template <int D, int NW, int RB, int KT>
-struct LoadMap {
-  int row[Shape<D, NW, RB, KT>::LOADS];
-  int col[Shape<D, NW, RB, KT>::LOADS];
-  __device__ __forceinline__ void init() {
-    using S = Shape<D, NW, RB, KT>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int j = 0; j < S::LOADS; ++j) {
-      const int seg = j * NW + wave;
-      const bool is_v = seg >= S::SEGK;
-      const int slots = is_v ? S::VSLOT : S::KSLOT;
-      const int q = (is_v ? seg - S::SEGK : seg) * 64 + lane;
-      const int c = q % slots;
-      row[j] = min(q / slots, KT - 1);
-      col[j] = c < D / 8 ? c * 8 : 0;
-    }
-  }
-};
-
-// K and V tile -> one LDS stage, no registers involved. Rows past `valid` repeat the last
-// valid row; those keys are masked in the scores, so their values only need to be finite.
-template <int D, int NW, int RB, int KT>
-__device__ __forceinline__ void load_tile(uint16_t* stage, const LoadMap<D, NW, RB, KT>& lm,
-                                          const KeySrc& src) {
-  using S = Shape<D, NW, RB, KT>;
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < S::LOADS; ++j) {
-    const int seg = j * NW + wave;
-    if (seg < S::SEG) {
-      const bool is_v = seg >= S::SEGK;
-      const int off = min(lm.row[j], src.valid - 1) * (int)src.stride + lm.col[j];
-      __builtin_amdgcn_global_load_lds((is_v ? src.v : src.k) + off, stage + seg * 512, 16, 0, 0);
-    }
-  }
-}
-
-// One key tile for one wave: S^T = K.Q^T, (masked) online softmax, O^T += V^T.P^T.
-template <int D, int NW, int RB, int KT, bool MASK>
-__device__ __forceinline__ void attend_tile(const uint16_t* stage, const bf16x8 (&qf)[RB][D / 16],
-                                            f32x16 (&o)[RB][D / 32], float (&m_run)[RB],
-                                            float (&l_run)[RB], float scale_log2, bool prefix,
-                                            int key0, int valid, int wrow0) {
-  using S = Shape<D, NW, RB, KT>;
-  constexpr int ND = D / 32, NK = D / 16, NN = KT / 32;
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5, l32 = lane & 31;
-  const f32x16 zero = {};
-
-  // S^T[key, row] for NN blocks of 32 keys; A = K rows from LDS, B = Q^T from registers
-  const uint16_t* kbase = stage + l32 * S::KSTR + half * 8;
-  f32x16 s[RB][NN];
-#pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
-#pragma unroll
-    for (int n = 0; n < NN; ++n) {
-      const bf16x8 a = as_bf16x8(load16(kbase + n * 32 * S::KSTR + ks * 16));
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        s[rb][n] = mfma32(a, qf[rb][ks], ks == 0 ? zero : s[rb][n]);
-    }
-  }
-
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (MASK) {
-      const int row = wrow0 + rb * 32 + l32;
-#pragma unroll
-      for (int n = 0; n < NN; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = n * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          const bool dead = prefix ? (kk >= valid) : (key0 + kk > row);
-          s[rb][n][r] = dead ? -INFINITY : s[rb][n][r];
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int n = 0; n < NN; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][n][r]);
-    mx = fmaxf(mx, swap_half(mx));
-    const float mxs = mx * scale_log2;
-    if (mxs > m_run[rb] + kLazyTau) {
-      if (m_run[rb] != -INFINITY) {     // the first visible tile needs no rescale (O = 0)
-        const float alpha = fast_exp2(m_run[rb] - mxs);
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
-      }
-      m_run[rb] = mxs;
-    }
-    const float mu = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-    float ls = 0.f;
-#pragma unroll
-    for (int n = 0; n < NN; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(s[rb][n][r], scale_log2, -mu));
-        ls += e;
-        s[rb][n][r] = e;
-      }
-    l_run[rb] += ls;
-  }
-
-  // O^T += V^T . P^T, 16 keys per MFMA. P^T element e of chunk c (lane half h) is key
-  // 16c + 8(e/4) + 4h + e%4 (the S^T register order); the V^T operand is fetched with two
-  // transposing reads: source lane j of each 16-lane group points at key row
-  // 16c + 8t + 4h + j/4 and d columns 32db + 16*(group % 2) + 4*(j % 4) .. +3.
-  const int grp = (lane >> 4) & 1, j16 = lane & 15;
-  const uint16_t* vbase = stage + S::VOFF + (4 * half + (j16 >> 2)) * S::VSTR + 16 * grp + 4 * (j16 & 3);
-#pragma unroll
-  for (int c = 0; c < KT / 16; ++c) {
-    bf16x8 pf[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const f32x16& sv = s[rb][c / 2];
-      const int b0 = (c % 2) * 8;
-      u32x4 w = {pack_bf16x2(sv[b0 + 0], sv[b0 + 1]), pack_bf16x2(sv[b0 + 2], sv[b0 + 3]),
-                 pack_bf16x2(sv[b0 + 4], sv[b0 + 5]), pack_bf16x2(sv[b0 + 6], sv[b0 + 7])};
-      pf[rb] = as_bf16x8(w);
-    }
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const uint16_t* src = vbase + 16 * c * S::VSTR + 32 * db;
-      const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-      const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * S::VSTR));
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      const s16x8 both = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-      const bf16x8 va = __builtin_bit_cast(bf16x8, both);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(va, pf[rb], o[rb][db]);
-    }
-  }
-}
+constexpr int kNoCausal = 1 << 30;   // position of a row that no causal source limits
 
 template <int D, int NW, int RB, int KT>
 __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, int v, int t,
@@ -291,12 +121,17 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, 
     const bool skip = !prefix && key0 > wrow0 + 32 * RB - 1;
     if (!skip) {
       const bool need_mask = prefix ? (valid < KT) : (key0 + KT - 1 > wrow0);
-      if (need_mask)
-        attend_tile<D, NW, RB, KT, true>(stage, qf, o, m_run, l_run, p.scale_log2, prefix, key0,
-                                         valid, wrow0);
-      else
-        attend_tile<D, NW, RB, KT, false>(stage, qf, o, m_run, l_run, p.scale_log2, prefix, key0,
-                                          valid, wrow0);
+      if (need_mask) {
+        int pos[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) pos[rb] = prefix ? kNoCausal : wrow0 + rb * 32 + l32;
+        attend_tile<D, NW, RB, KT, true>(stage, qf, o, m_run, l_run, p.scale_log2, key0, valid,
+                                         pos);
+      } else {
+        const int pos[RB] = {};
+        attend_tile<D, NW, RB, KT, false>(stage, qf, o, m_run, l_run, p.scale_log2, key0,
+                                          valid, pos);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -346,47 +181,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   }
 }
 
-// Kernel variant: NW waves per workgroup, 32*RB rows per wave, KT keys per tile.
-// APBV_ATTN_CFG = "NWxRBxKT" ("8x1x64", "4x1x64", "4x2x64") overrides the default for
-// tuning runs.
-struct Cfg {
-  int nw, rb, kt;
-};
-Cfg config() {
-  static const Cfg c = [] {
-    const Cfg def = {8, 1, 64};
-    const char* e = getenv("APBV_ATTN_CFG");
-    if (e == nullptr) return def;
-    const Cfg known[] = {{4, 2, 64}, {4, 1, 64}, {8, 1, 64}};
-    for (const Cfg& k : known) {
-      char buf[16];
-      snprintf(buf, sizeof(buf), "%dx%dx%d", k.nw, k.rb, k.kt);
-      if (strcmp(buf, e) == 0) return k;
-    }
-    return def;
-  }();
-  return c;
-}
-
-template <int D, int NW, int RB, int KT>
-void launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_kernel<D, NW, RB, KT>), grid, dim3(NW * 64), 0, stream, p);
-}
+// One workgroup = 8 waves x 32 query rows (two waves per SIMD), 64-key tiles.
+constexpr int kWaves = 8, kRowBlocks = 1, kKeys = 64;
 
 template <int D>
 hipError_t launch_d(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  const Cfg c = config();
-  if (c.nw == 4 && c.rb == 2) launch_one<D, 4, 2, 64>(p, grid, stream);
-  else if (c.nw == 4) launch_one<D, 4, 1, 64>(p, grid, stream);
-  else launch_one<D, 8, 1, 64>(p, grid, stream);
+  hipLaunchKernelGGL((attn_kernel<D, kWaves, kRowBlocks, kKeys>), grid, dim3(kWaves * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int attn_tile_rows(int head_dim) {
-  const Cfg c = config();
-  return (head_dim == 64 || head_dim == 128) ? c.nw * 32 * c.rb : 0;
+  return (head_dim == 64 || head_dim == 128) ? kWaves * 32 * kRowBlocks : 0;
 }
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream) {

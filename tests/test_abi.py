@@ -98,6 +98,47 @@ def test_invalid_pointers_and_ranges():
     assert L.apbv_status_str(3).decode().startswith("workspace")
 
 
+def call_query(layout, ws_bytes=None, **ptrs):
+    p = dict(qq=0x1000, kq=0x2000, vq=0x3000, ka=0x4000, va=0x5000, kc=0x6000, vc=0x7000,
+             out=0x8000, lse=None, ws=0x10000)
+    p.update(ptrs)
+    L = apbv.lib()
+    if ws_bytes is None:
+        n = ctypes.c_size_t(0)
+        assert L.apbv_query_forward_workspace(layout.ref(), ctypes.byref(n)) == 0
+        ws_bytes = n.value
+    return L.apbv_query_forward(layout.ref(), p["qq"], p["kq"], p["vq"], p["ka"], p["va"],
+                                p["kc"], p["vc"], p["out"], p["lse"], p["ws"], ws_bytes, None)
+
+
+def test_query_forward_validation():
+    lay = small_layout()                              # N=900, l_a=64, l_q=32, hq=4, d=128
+    L = apbv.lib()
+    n = ctypes.c_size_t(0)
+    assert L.apbv_query_forward_workspace(lay.ref(), ctypes.byref(n)) == 0
+    # chunks: 1 anchor + 1 context (<= 4096 keys each) + 1 query; fp32 outputs and lse
+    chunks = 3
+    o_bytes = -(-chunks * 4 * 32 * 128 * 4 // 256) * 256
+    lse_bytes = -(-chunks * 4 * 32 * 4 // 256) * 256
+    assert n.value == o_bytes + lse_bytes
+    assert call_query(lay, qq=None) == _lib.APBV_EINVAL
+    assert call_query(lay, kq=None) == _lib.APBV_EINVAL
+    assert call_query(lay, va=None) == _lib.APBV_EINVAL       # anchor present
+    assert call_query(lay, out=0x8008) == _lib.APBV_EINVAL    # misaligned
+    assert call_query(lay, lse=0x9002) == _lib.APBV_EINVAL
+    assert call_query(lay, ws=0x10010) == _lib.APBV_EINVAL    # workspace not 256-aligned
+    assert call_query(lay, ws_bytes=n.value - 1) == _lib.APBV_EWORKSPACE
+    assert call_query(lay, ws=None) == _lib.APBV_EWORKSPACE
+    assert call_query(small_layout(head_dim=96), ws_bytes=1 << 20) == _lib.APBV_EUNSUPPORTED
+    # no query rows: nothing to do, nothing needed
+    empty = small_layout(l_query=0)
+    assert L.apbv_query_forward_workspace(empty.ref(), ctypes.byref(n)) == 0 and n.value == 0
+    assert call_query(empty, ws_bytes=0, qq=None, kq=None, vq=None, out=None, ws=None) == 0
+    # no anchor: the anchor pointers may be NULL
+    st = call_query(small_layout(l_anchor=0), ka=None, va=None, ws=None, ws_bytes=0)
+    assert st == _lib.APBV_EWORKSPACE                          # only the workspace is missing
+
+
 def rows_per_tile():
     return apbv.attn_tile_rows(128)
 
