@@ -45,7 +45,8 @@ constexpr int kNoCausal = 1 << 30;   // position of a row that no causal source 
 
 template <int D, int NW, int RB, int KT>
 __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, int v, int t,
-                                             uint16_t* lds, const LoadMap<D, NW, RB, KT>& lm) {
+                                             uint16_t* lds0, uint16_t* lds1,
+                                             const LoadMap<D, NW, RB, KT>& lm) {
   using S = Shape<D, NW, RB, KT>;
   constexpr int M = S::M;
   constexpr int ND = D / 32;     // 32-wide d blocks of O^T
@@ -106,14 +107,12 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, 
     return s;
   };
 
-  load_tile<D, NW, RB, KT>(lds, lm, source(0));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int i = 0; i < ntiles; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < ntiles) load_tile<D, NW, RB, KT>(lds + (buf ^ 1) * S::STAGE, lm, source(i + 1));
-    const uint16_t* stage = lds + buf * S::STAGE;
+  // Tile i is read from stage i % 2 while tile i + 1 streams into the other stage. The two
+  // stages are separate LDS arrays and the loop is unrolled by two, so every LDS access
+  // names its array statically: the compiler can then tell the reads of one stage from the
+  // direct-to-LDS loads into the other and does not wait for those loads before reading.
+  auto step = [&](int i, const uint16_t* stage, uint16_t* next) {
+    if (i + 1 < ntiles) load_tile<D, NW, RB, KT>(next, lm, source(i + 1));
     const bool prefix = i < n_pre;
     const int key0 = prefix ? i * KT : lo + (i - n_pre) * KT;
     const int valid = prefix ? min(KT, P - key0) : min(KT, r1 - key0);
@@ -135,6 +134,14 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, 
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  load_tile<D, NW, RB, KT>(lds0, lm, source(0));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = 0; i < ntiles; i += 2) {
+    step(i, lds0, lds1);
+    if (i + 1 < ntiles) step(i + 1, lds1, lds0);
   }
 
   // epilogue: O = O^T / l, bf16; lse = (m + log2 l) * ln 2
@@ -163,7 +170,8 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, 
 
 template <int D, int NW, int RB, int KT>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * Shape<D, NW, RB, KT>::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds0[Shape<D, NW, RB, KT>::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds1[Shape<D, NW, RB, KT>::STAGE];
   LoadMap<D, NW, RB, KT> lm;
   lm.init();
   const uint32_t total = (uint32_t)p.n_units * (uint32_t)p.hq;
@@ -177,7 +185,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   for (int part = 0; part < 2; ++part) {
     const int v = part == 0 ? va : vb;
     const int t = part == 0 ? ta : tb;
-    if (v >= 0) process_tile<D, NW, RB, KT>(p, h, g, v, t, lds, lm);
+    if (v >= 0) process_tile<D, NW, RB, KT>(p, h, g, v, t, lds0, lds1, lm);
   }
 }
 

@@ -68,20 +68,32 @@ struct LoadMap {
   }
 };
 
-// K and V tile -> one LDS stage, no registers involved. Rows past `valid` repeat the last
+// Raw buffer descriptor over the rows of one tile (the byte offsets of a tile stay far
+// below 2^31; the third-dword value is the gfx9 raw-buffer format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, 0x7fffffff,
+                                           0x00020000);
+}
+
+// K and V tile -> one LDS stage, no registers involved (buffer loads that write LDS: unlike
+// the global form they leave the LDS-read counter to the LDS reads, so the reads of the
+// current tile can wait for one another one at a time). Rows past `valid` repeat the last
 // valid row; those keys are masked in the scores, so their values only need to be finite.
 template <int D, int NW, int RB, int KT>
 __device__ __forceinline__ void load_tile(uint16_t* stage, const LoadMap<D, NW, RB, KT>& lm,
                                           const KeySrc& src) {
   using S = Shape<D, NW, RB, KT>;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(src.k), rv = tile_rsrc(src.v);
 #pragma unroll
   for (int j = 0; j < S::LOADS; ++j) {
     const int seg = j * NW + wave;
     if (seg < S::SEG) {
       const bool is_v = seg >= S::SEGK;
-      const int off = min(lm.row[j], src.valid - 1) * (int)src.stride + lm.col[j];
-      __builtin_amdgcn_global_load_lds((is_v ? src.v : src.k) + off, stage + seg * 512, 16, 0, 0);
+      const int off = (min(lm.row[j], src.valid - 1) * (int)src.stride + lm.col[j]) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          is_v ? rv : rk, (__attribute__((address_space(3))) void*)(stage + seg * 512), 16, off,
+          0, 0, 0);
     }
   }
 }
@@ -102,13 +114,14 @@ __device__ __forceinline__ void attend_tile(const uint16_t* stage, const bf16x8 
   const f32x16 zero = {};
 
   // S^T[key, row] for NN blocks of 32 keys; A = K rows from LDS, B = Q^T from registers
-  const uint16_t* kbase = stage + l32 * S::KSTR + half * 8;
+  int kofs = l32 * S::KSTR + half * 8;
+  asm volatile("" : "+v"(kofs));
   f32x16 s[RB][NN];
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) {
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
-      const bf16x8 a = as_bf16x8(load16(kbase + n * 32 * S::KSTR + ks * 16));
+      const bf16x8 a = as_bf16x8(load16(stage + (kofs + n * 32 * S::KSTR + ks * 16)));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         s[rb][n] = mfma32(a, qf[rb][ks], ks == 0 ? zero : s[rb][n]);
@@ -163,7 +176,8 @@ __device__ __forceinline__ void attend_tile(const uint16_t* stage, const bf16x8 
   // transposing reads: source lane j of each 16-lane group points at key row
   // 16c + 8t + 4h + j/4 and d columns 32db + 16*(group % 2) + 4*(j % 4) .. +3.
   const int grp = (lane >> 4) & 1, j16 = lane & 15;
-  const uint16_t* vbase = stage + S::VOFF + (4 * half + (j16 >> 2)) * S::VSTR + 16 * grp + 4 * (j16 & 3);
+  int vofs = S::VOFF + (4 * half + (j16 >> 2)) * S::VSTR + 16 * grp + 4 * (j16 & 3);
+  asm volatile("" : "+v"(vofs));
 #pragma unroll
   for (int c = 0; c < KT / 16; ++c) {
     bf16x8 pf[RB];
@@ -177,9 +191,9 @@ __device__ __forceinline__ void attend_tile(const uint16_t* stage, const bf16x8 
     }
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
-      const uint16_t* src = vbase + 16 * c * S::VSTR + 32 * db;
-      const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-      const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 8 * S::VSTR));
+      const int o0 = vofs + 16 * c * S::VSTR + 32 * db;
+      const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(stage + o0));
+      const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(stage + (o0 + 8 * S::VSTR)));
       typedef short s16x8 __attribute__((ext_vector_type(8)));
       const s16x8 both = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       const bf16x8 va = __builtin_bit_cast(bf16x8, both);
