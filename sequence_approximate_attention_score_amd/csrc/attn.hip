@@ -7,8 +7,8 @@
 // Approssimata"; with one block and no prefix this is plain causal flash attention, as the
 // page's "Limitazioni" paragraph notes).
 //
-// Design (one workgroup = 8 waves = one query tile of 256 rows of one head,
-// 32 rows per wave, two waves per SIMD so one wave's softmax overlaps the other's MFMAs):
+// Design (one workgroup = 8 waves = one query tile of 256 rows of one head, 32 rows per
+// wave, two waves per SIMD):
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: the K tile (shared by the waves) is the A
 //    operand read from LDS, the wave's Q rows are the B operand held in registers. The
 //    result puts one query row per lane (lanes l and l+32 share a row and split its keys),
@@ -16,15 +16,19 @@
 //  * O^T = V^T . P^T: the probabilities are already laid out as the B operand; the V^T
 //    operand comes straight from a row-major V tile through ds_read_b64_tr_b16 (two
 //    transposing 8-byte reads per operand), so the rescale factor of a row is lane-local.
-//  * K and V tiles of 64 keys go global -> LDS with global_load_lds_dwordx4 (no register
-//    staging) into padded rows (K: +16 B, V: +32 B), which keeps the 128-bit operand reads
-//    and the transposing reads near the LDS peak while every LDS read address is a per-lane
-//    base plus a compile-time offset; double-buffered, the next tile's loads in flight
-//    while the current one is computed, one barrier per tile.
+//  * Software pipeline inside each wave: while the exponentials of tile i are computed on
+//    the vector ALU, the matrix core already computes the scores of tile i + 1; then
+//    O += V_i^T P_i^T runs beside the row sums of tile i and the row maxima of tile i + 1.
+//    The instruction order is fixed with scheduling groups so that every MFMA has vector
+//    work issued behind it. K tiles therefore run one tile ahead of V tiles: two K buffers
+//    and two V buffers (separate LDS arrays, padded rows: K +16 B, V +32 B), filled by
+//    buffer loads straight into LDS; the loads of K_{i+2} and V_{i+1} are in flight during
+//    iteration i, one barrier per iteration. The loop is unrolled by two so that every LDS
+//    access names its array statically.
 //  * Online softmax in log2 units with a lazy rescale: the running offset is only raised
 //    when a tile's maximum exceeds it by more than 8 (probabilities stay <= 256), which is
-//    exact up to rounding and skips almost every O rescale. Masking code runs only on
-//    tiles that need it (ragged prefix end, causal diagonal).
+//    exact up to rounding and skips almost every O rescale. Mask code runs only on tiles
+//    that need it (ragged prefix end, causal diagonal).
 //  * Grid = work units x heads, remapped so each XCD gets a contiguous range: the heads of
 //    one KV group and one unit run side by side on the same XCD and share K/V in its L2.
 #include "apbv_device.h"
@@ -35,145 +39,349 @@ namespace apbv {
 
 namespace {
 
-using tile::attend_tile;
 using tile::KeySrc;
-using tile::load_tile;
-using tile::LoadMap;
-using tile::Shape;
+using tile::tile_rsrc;
 
-constexpr int kNoCausal = 1 << 30;   // position of a row that no causal source limits
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, int NW, int RB, int KT>
+constexpr int kWaves = 8;             // 32 query rows each, two per SIMD
+constexpr int kKT = 64;               // keys per tile
+constexpr int kRows = kWaves * 32;    // query rows per work tile
+constexpr int kNoCausal = 1 << 30;    // position of a row that no causal source limits
+constexpr float kTau = 8.0f;          // log2 headroom before the running offset is raised
+
+// sched_group_barrier classes
+constexpr int kSchedVALU = 0x2, kSchedMFMA = 0x8, kSchedDSRead = 0x100;
+
+template <int D>
+struct Geo {
+  static constexpr int KSTR = D + 8;               // K row stride in LDS (elements)
+  static constexpr int VSTR = D + 16;              // V row stride in LDS (elements)
+  static constexpr int KSLOT = KSTR / 8;           // 16-byte slots per padded row
+  static constexpr int VSLOT = VSTR / 8;
+  static constexpr int SEGK = kKT * KSLOT / 64;    // 1 KB load segments per K tile
+  static constexpr int SEGV = kKT * VSLOT / 64;
+  static constexpr int KELEMS = SEGK * 512;        // elements per K buffer
+  static constexpr int VELEMS = SEGV * 512;
+  // waves 0..3 load K tiles, waves 4..7 load V tiles
+  static constexpr int LOADS = ((SEGK > SEGV ? SEGK : SEGV) + 3) / 4;
+  static constexpr int NK = D / 16;                // 16-deep k steps of S^T
+  static constexpr int ND = D / 32;                // 32-wide d blocks of O^T
+};
+
+// Per-lane source row / column of each load slot of this wave's half (K or V); padding
+// slots repeat column 0 of their row.
+template <int D>
+struct Loader {
+  int rc[Geo<D>::LOADS];   // row << 16 | column
+  int wave4;        // wave index within its half (uniform)
+  bool is_v;        // this wave loads V tiles (uniform)
+  __device__ __forceinline__ void init() {
+    using G = Geo<D>;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    is_v = wave >= 4;
+    wave4 = wave & 3;
+    const int slots = is_v ? G::VSLOT : G::KSLOT;
+#pragma unroll
+    for (int j = 0; j < G::LOADS; ++j) {
+      const int q = (j * 4 + wave4) * 64 + lane;
+      const int c = q % slots;
+      rc[j] = (min(q / slots, kKT - 1) << 16) | (c < D / 8 ? c * 8 : 0);
+    }
+  }
+  // One tile (K or V rows from `base`, row stride `stride`, `valid` rows) into `dst`.
+  // Rows past `valid` repeat the last valid row (masked later, only need to be finite).
+  template <int SEGS>
+  __device__ __forceinline__ void load(uint16_t* dst, const uint16_t* base, int64_t stride,
+                                       int valid) const {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base);
+#pragma unroll
+    for (int j = 0; j < Geo<D>::LOADS; ++j) {
+      const int seg = j * 4 + wave4;
+      if (seg < SEGS) {
+        const int off = (min(rc[j] >> 16, valid - 1) * (int)stride + (rc[j] & 0xffff)) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + seg * 512), 16, off, 0,
+                                                 0, 0);
+      }
+    }
+  }
+};
+
+// Scores s[n] (keys 32n .. 32n+31 of the tile, rows = the wave's 32 query rows) of one
+// K tile, as 16 MFMAs.
+template <int D>
+__device__ __forceinline__ void tile_scores(const uint16_t* kbuf, int kofs,
+                                            const bf16x8 (&qf)[D / 16], f32x16 (&s)[2]) {
+  using G = Geo<D>;
+  const f32x16 zero = {};
+#pragma unroll
+  for (int ks = 0; ks < G::NK; ++ks)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const bf16x8 a = as_bf16x8(load16(kbuf + (kofs + n * 32 * G::KSTR + ks * 16)));
+      s[n] = mfma32(a, qf[ks], ks == 0 ? zero : s[n]);
+    }
+}
+
+// Keys past `valid` or, for causal rows, past the row's own position become -inf.
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int key0, int valid, int pos) {
+  const int half = (threadIdx.x & 63) >> 5;
+  const int lim = min(valid - 1, pos - key0);   // last visible key of the tile
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = n * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+      s[n][r] = kk > lim ? -INFINITY : s[n][r];
+    }
+}
+
+__device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
+  return fmaxf(mx, swap_half(mx));
+}
+
+// One pipelined iteration for tile i (its scores in sc, row max mx): exponentials of tile i
+// beside the scores of tile i + 1 (into sn, from kbuf), then O += V_i^T P_i^T beside the row
+// sum of tile i and the row max of tile i + 1 (into mx_next). A tile with masked keys is
+// masked here, before its row max is taken again; branches come first so that the two
+// phases form one straight-line block whose instruction order the scheduling groups fix.
+template <int D>
+__device__ __forceinline__ void pipe_step(const uint16_t* kbuf, const uint16_t* vbuf, int kofs,
+                                          int vofs, const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&o)[D / 32], f32x16 (&sc)[2], f32x16 (&sn)[2],
+                                          float& mx, float& m_run, float& l_run,
+                                          float scale_log2, bool mask, int key0, int valid,
+                                          int pos) {
+  using G = Geo<D>;
+  if (mask) {
+    mask_scores(sc, key0, valid, pos);
+    mx = row_max(sc);
+  }
+  // lazy rescale of the running state (rare: taken when the row maximum grows by > kTau)
+  const float mxs = mx * scale_log2;
+  if (mxs > m_run + kTau) {
+    if (m_run != -INFINITY) {     // the first visible tile needs no rescale (O = 0)
+      const float alpha = fast_exp2(m_run - mxs);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < G::ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    m_run = mxs;
+  }
+  const float mu = m_run == -INFINITY ? 0.f : m_run;
+
+  // phase A: P_i = exp2(scale * S_i - m) packed to bf16, beside S_{i+1} = K_{i+1} Q^T
+  bf16x8 pf[4];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[n][r] = fast_exp2(fmaf(sc[n][r], scale_log2, -mu));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const f32x16& sv = sc[c / 2];
+    const int b0 = (c % 2) * 8;
+    u32x4 w = {pack_bf16x2(sv[b0 + 0], sv[b0 + 1]), pack_bf16x2(sv[b0 + 2], sv[b0 + 3]),
+               pack_bf16x2(sv[b0 + 4], sv[b0 + 5]), pack_bf16x2(sv[b0 + 6], sv[b0 + 7])};
+    pf[c] = as_bf16x8(w);
+  }
+  tile_scores<D>(kbuf, kofs, qf, sn);
+
+  // phase B: O^T += V_i^T P_i^T (16 keys per MFMA; P^T element e of chunk c in lane half h
+  // is key 16c + 8(e/4) + 4h + e%4, and the V^T operand is fetched with two transposing
+  // reads whose source lane j of each 16-lane group points at key row 16c + 8t + 4h + j/4
+  // and d columns 32db + 16*(group % 2) + 4*(j % 4) .. +3), beside the row sum of P_i and
+  // the row max of S_{i+1}
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int db = 0; db < G::ND; ++db) {
+      const int o0 = vofs + 16 * c * G::VSTR + 32 * db;
+      const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbuf + o0));
+      const s16x4 p1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbuf + (o0 + 8 * G::VSTR)));
+      const s16x8 both = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      o[db] = mfma32(__builtin_bit_cast(bf16x8, both), pf[c], o[db]);
+    }
+  float ls = 0.f;
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ls += sc[n][r];
+  l_run += ls;
+  mx = row_max(sn);
+
+  // instruction order: phase A = per S MFMA one K read (two ahead) and 5 vector ops,
+  // phase B = per PV MFMA two transposing reads (four ahead) and 3 vector ops
+  __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+#pragma unroll
+  for (int j = 0; j < 2 * G::NK; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+    if (j + 2 < 2 * G::NK) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVALU, 5, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+  for (int j = 0; j < 4 * G::ND; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+    if (j + 2 < 4 * G::ND) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
+  }
+}
+
+template <int D>
 __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, int v, int t,
-                                             uint16_t* lds0, uint16_t* lds1,
-                                             const LoadMap<D, NW, RB, KT>& lm) {
-  using S = Shape<D, NW, RB, KT>;
-  constexpr int M = S::M;
-  constexpr int ND = D / 32;     // 32-wide d blocks of O^T
-  constexpr int NK = D / 16;     // 16-deep k steps of S^T
-
+                                             uint16_t* K0, uint16_t* K1, uint16_t* V0,
+                                             uint16_t* V1, const Loader<D>& ld) {
+  using G = Geo<D>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int lo = p.sched.bs[v], hi = p.sched.bs[v + 1];
-  const int r0 = lo + t * M;
-  const int r1 = min(r0 + M, hi);
-  const int wrow0 = r0 + wave * 32 * RB;   // first row of this wave
+  const int r0 = lo + t * kRows;
+  const int r1 = min(r0 + kRows, hi);
+  const int wrow0 = r0 + wave * 32;          // first row of this wave
+  const int row = wrow0 + l32;
 
-  // Q^T fragments (B operand): lane holds row l32 of each row block, d = 16ks + 8half + e.
-  // Rows past the tile end repeat a valid row; their outputs are never stored.
-  bf16x8 qf[RB][NK];
+  // Q^T fragments (B operand): lane holds row l32, d = 16ks + 8half + e. Rows past the
+  // tile end repeat a valid row; their outputs are never stored.
+  bf16x8 qf[G::NK];
+  {
+    const uint16_t* qrow = p.q + (int64_t)min(row, r1 - 1) * p.q_stride + h * D + half * 8;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = min(wrow0 + rb * 32 + l32, r1 - 1);
-    const uint16_t* qrow = p.q + (int64_t)row * p.q_stride + h * D + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) qf[rb][ks] = as_bf16x8(load16(qrow + ks * 16));
+    for (int ks = 0; ks < G::NK; ++ks) qf[ks] = as_bf16x8(load16(qrow + ks * 16));
   }
-
-  f32x16 o[RB][ND];
-  float m_run[RB], l_run[RB];
+  f32x16 o[G::ND];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.f;
+  for (int db = 0; db < G::ND; ++db)
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
   const int P = p.l_anchor + v * p.l_pass;
-  const int n_pre = (P + KT - 1) / KT;
-  const int n_loc = (r1 - lo + KT - 1) / KT;
+  const int n_pre = (P + kKT - 1) / kKT;
+  const int n_loc = (r1 - lo + kKT - 1) / kKT;
   const int ntiles = n_pre + n_loc;
+  // tiles this wave computes: every prefix tile, and local tiles up to its last row
+  const int n_live = n_pre + min(n_loc, (wrow0 + 31 - lo) / kKT + 1);
 
   auto source = [&](int i) -> KeySrc {
     KeySrc s;
     if (i < n_pre) {
-      const int key0 = i * KT;
+      const int key0 = i * kKT;
       const int64_t off = ((int64_t)g * p.pre_rows + key0) * D;
       s.k = p.kpre + off;
       s.v = p.vpre + off;
       s.stride = D;
-      s.valid = min(KT, P - key0);
+      s.valid = min(kKT, P - key0);
     } else {
-      const int key0 = lo + (i - n_pre) * KT;
+      const int key0 = lo + (i - n_pre) * kKT;
       const int64_t off = (int64_t)key0 * p.kv_stride + g * D;
       s.k = p.kc + off;
       s.v = p.vc + off;
       s.stride = p.kv_stride;
-      s.valid = min(KT, r1 - key0);
+      s.valid = min(kKT, r1 - key0);
     }
     return s;
   };
-
-  // Tile i is read from stage i % 2 while tile i + 1 streams into the other stage. The two
-  // stages are separate LDS arrays and the loop is unrolled by two, so every LDS access
-  // names its array statically: the compiler can then tell the reads of one stage from the
-  // direct-to-LDS loads into the other and does not wait for those loads before reading.
-  auto step = [&](int i, const uint16_t* stage, uint16_t* next) {
-    if (i + 1 < ntiles) load_tile<D, NW, RB, KT>(next, lm, source(i + 1));
-    const bool prefix = i < n_pre;
-    const int key0 = prefix ? i * KT : lo + (i - n_pre) * KT;
-    const int valid = prefix ? min(KT, P - key0) : min(KT, r1 - key0);
-    // a local tile entirely in the future of every row of this wave adds nothing
-    const bool skip = !prefix && key0 > wrow0 + 32 * RB - 1;
-    if (!skip) {
-      const bool need_mask = prefix ? (valid < KT) : (key0 + KT - 1 > wrow0);
-      if (need_mask) {
-        int pos[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) pos[rb] = prefix ? kNoCausal : wrow0 + rb * 32 + l32;
-        attend_tile<D, NW, RB, KT, true>(stage, qf, o, m_run, l_run, p.scale_log2, key0, valid,
-                                         pos);
-      } else {
-        const int pos[RB] = {};
-        attend_tile<D, NW, RB, KT, false>(stage, qf, o, m_run, l_run, p.scale_log2, key0,
-                                          valid, pos);
-      }
+  // mask parameters of tile i: first key position, valid keys, whether any key of this
+  // wave's rows is masked, and the lane's causal position
+  auto key0_of = [&](int i) { return i < n_pre ? i * kKT : lo + (i - n_pre) * kKT; };
+  auto valid_of = [&](int i) {
+    return i < n_pre ? min(kKT, P - i * kKT) : min(kKT, r1 - key0_of(i));
+  };
+  auto needs_mask = [&](int i) {
+    return i < n_pre ? valid_of(i) < kKT : key0_of(i) + kKT - 1 > wrow0;
+  };
+  auto pos_of = [&](int i) { return i < n_pre ? kNoCausal : row; };
+  auto load_k = [&](uint16_t* dst, int i) {
+    if (!ld.is_v && i < ntiles) {
+      const KeySrc s = source(i);
+      ld.template load<G::SEGK>(dst, s.k, s.stride, s.valid);
     }
+  };
+  auto load_v = [&](uint16_t* dst, int i) {
+    if (ld.is_v && i < ntiles) {
+      const KeySrc s = source(i);
+      ld.template load<G::SEGV>(dst, s.v, s.stride, s.valid);
+    }
+  };
+
+  int kofs = l32 * G::KSTR + half * 8;
+  const int grp = (lane >> 4) & 1, j16 = lane & 15;
+  int vofs = (4 * half + (j16 >> 2)) * G::VSTR + 16 * grp + 4 * (j16 & 3);
+  // opaque lane offsets: every LDS read address stays "array + offset + constant", which
+  // keeps the array's alias information on the read
+  asm volatile("" : "+v"(kofs), "+v"(vofs));
+
+  // prologue: K_0, V_0, K_1 in flight; scores of tile 0
+  load_k(K0, 0);
+  load_v(V0, 0);
+  load_k(K1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  tile_scores<D>(K0, kofs, qf, sa);
+  float mx = row_max(sa);
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sb[n][r] = 0.f;
+  __syncthreads();   // K0 is refilled by iteration 0
+
+  // iteration i reads K_{i+1} and V_i and refills the buffers of K_i and V_{i-1}
+  auto iter = [&](int i, const uint16_t* kread, const uint16_t* vread, uint16_t* kload,
+                  uint16_t* vload, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    load_k(kload, i + 2);
+    load_v(vload, i + 1);
+    if (i < n_live)
+      pipe_step<D>(kread, vread, kofs, vofs, qf, o, sc, sn, mx, m_run, l_run, p.scale_log2,
+                   needs_mask(i), key0_of(i), valid_of(i), pos_of(i));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-
-  load_tile<D, NW, RB, KT>(lds0, lm, source(0));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   for (int i = 0; i < ntiles; i += 2) {
-    step(i, lds0, lds1);
-    if (i + 1 < ntiles) step(i + 1, lds1, lds0);
+    iter(i, K1, V0, K0, V1, sa, sb);
+    if (i + 1 < ntiles) iter(i + 1, K0, V1, K1, V0, sb, sa);
   }
 
   // epilogue: O = O^T / l, bf16; lse = (m + log2 l) * ln 2
+  const float lt = l_run + swap_half(l_run);
+  if (row < r1) {
+    const float inv = 1.0f / lt;
+    uint16_t* orow = p.out + ((int64_t)row * p.hq + h) * D;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float lt = l_run[rb] + swap_half(l_run[rb]);
-    const int row = wrow0 + rb * 32 + l32;
-    if (row < r1) {
-      const float inv = 1.0f / lt;
-      uint16_t* orow = p.out + ((int64_t)row * p.hq + h) * D;
+    for (int db = 0; db < G::ND; ++db)
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = db * 32 + 8 * q4 + 4 * half;
-          const f32x16& ov = o[rb][db];
-          u32x2 w = {pack_bf16x2(ov[4 * q4 + 0] * inv, ov[4 * q4 + 1] * inv),
-                     pack_bf16x2(ov[4 * q4 + 2] * inv, ov[4 * q4 + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + d0) = w;
-        }
-      if (p.lse != nullptr && half == 0)
-        p.lse[(int64_t)h * p.n_tokens + row] = (m_run[rb] + fast_log2(lt)) * 0.69314718055994531f;
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = db * 32 + 8 * q4 + 4 * half;
+        const f32x16& ov = o[db];
+        u32x2 w = {pack_bf16x2(ov[4 * q4 + 0] * inv, ov[4 * q4 + 1] * inv),
+                   pack_bf16x2(ov[4 * q4 + 2] * inv, ov[4 * q4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      }
+    if (p.lse != nullptr && half == 0)
+      p.lse[(int64_t)h * p.n_tokens + row] = (m_run + fast_log2(lt)) * 0.69314718055994531f;
   }
 }
 
-template <int D, int NW, int RB, int KT>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds0[Shape<D, NW, RB, KT>::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds1[Shape<D, NW, RB, KT>::STAGE];
-  LoadMap<D, NW, RB, KT> lm;
-  lm.init();
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void attn_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[Geo<D>::KELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t K1[Geo<D>::KELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[Geo<D>::VELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t V1[Geo<D>::VELEMS];
+  Loader<D> ld;
+  ld.init();
   const uint32_t total = (uint32_t)p.n_units * (uint32_t)p.hq;
   const uint32_t L = xcd_contiguous(blockIdx.x, total);
   const int unit = p.unit_begin + (int)(L / p.hq);
@@ -185,32 +393,27 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   for (int part = 0; part < 2; ++part) {
     const int v = part == 0 ? va : vb;
     const int t = part == 0 ? ta : tb;
-    if (v >= 0) process_tile<D, NW, RB, KT>(p, h, g, v, t, lds0, lds1, lm);
+    if (v >= 0) {
+      process_tile<D>(p, h, g, v, t, K0, K1, V0, V1, ld);
+      __syncthreads();   // the next part refills the buffers
+    }
   }
-}
-
-// One workgroup = 8 waves x 32 query rows (two waves per SIMD), 64-key tiles.
-constexpr int kWaves = 8, kRowBlocks = 1, kKeys = 64;
-
-template <int D>
-hipError_t launch_d(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_kernel<D, kWaves, kRowBlocks, kKeys>), grid, dim3(kWaves * 64), 0,
-                     stream, p);
-  return hipGetLastError();
 }
 
 }  // namespace
 
-int attn_tile_rows(int head_dim) {
-  return (head_dim == 64 || head_dim == 128) ? kWaves * 32 * kRowBlocks : 0;
-}
+int attn_tile_rows(int head_dim) { return (head_dim == 64 || head_dim == 128) ? kRows : 0; }
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t stream) {
   const uint64_t total = (uint64_t)p.n_units * (uint64_t)p.hq;
   if (total == 0) return hipSuccess;
   if (p.sched.tile_rows != attn_tile_rows(head_dim)) return hipErrorInvalidValue;
   const dim3 grid((uint32_t)total);
-  return head_dim == 128 ? launch_d<128>(p, grid, stream) : launch_d<64>(p, grid, stream);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(kWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace apbv
