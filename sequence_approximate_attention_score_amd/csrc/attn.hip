@@ -76,7 +76,8 @@ struct Geo {
 // slots repeat column 0 of their row.
 template <int D>
 struct Loader {
-  int rc[Geo<D>::LOADS];   // row << 16 | column
+  int row[Geo<D>::LOADS];    // source row of the slot
+  int colb[Geo<D>::LOADS];   // byte offset of the slot inside its row
   int wave4;        // wave index within its half (uniform)
   bool is_v;        // this wave loads V tiles (uniform)
   __device__ __forceinline__ void init() {
@@ -90,20 +91,23 @@ struct Loader {
     for (int j = 0; j < G::LOADS; ++j) {
       const int q = (j * 4 + wave4) * 64 + lane;
       const int c = q % slots;
-      rc[j] = (min(q / slots, kKT - 1) << 16) | (c < D / 8 ? c * 8 : 0);
+      row[j] = min(q / slots, kKT - 1);
+      colb[j] = c < D / 8 ? c * 16 : 0;
     }
   }
-  // One tile (K or V rows from `base`, row stride `stride`, `valid` rows) into `dst`.
-  // Rows past `valid` repeat the last valid row (masked later, only need to be finite).
+  // One tile (K or V rows from `base`, row stride `stride` elements, `valid` rows) into
+  // `dst`. Rows past `valid` repeat the last valid row (masked later, only need to be
+  // finite). Byte offsets are 24-bit products: a tile spans at most 64 rows of < 2^17 bytes.
   template <int SEGS>
   __device__ __forceinline__ void load(uint16_t* dst, const uint16_t* base, int64_t stride,
                                        int valid) const {
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base);
+    const unsigned stride_b = (unsigned)stride * 2u;
 #pragma unroll
     for (int j = 0; j < Geo<D>::LOADS; ++j) {
       const int seg = j * 4 + wave4;
       if (seg < SEGS) {
-        const int off = (min(rc[j] >> 16, valid - 1) * (int)stride + (rc[j] & 0xffff)) * 2;
+        const int off = (int)__umul24((unsigned)min(row[j], valid - 1), stride_b) + colb[j];
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + seg * 512), 16, off, 0,
                                                  0, 0);
       }
