@@ -5,7 +5,8 @@ One step = one layer of the hot path on the 128K-token Qwen2.5-VL-7B-shaped work
 anchor 2048, query block 128, l_p 1024): score_select -> gather_passing ->
 approx_attn_prefill, with every input already resident in HBM. Prints one JSON line.
 Beside the timed steps it also times the query block's rows (query_forward), each ZigZag
-bucket's attention alone, and the attention with the last-level cache flushed.
+bucket's attention alone, the attention with the last-level cache flushed, and one layer
+for each layout of the bucket sweep (2, 4, 6, 8 buckets) and of the anchor-only baseline.
 
     python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
                     [--profile] [--calib-copy]
@@ -166,7 +167,7 @@ def main():
 
     import torch
     import sequence_approximate_attention_score_amd as apbv
-    from synthetic import generate, workload
+    from synthetic import generate, sweep_layouts, workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -234,6 +235,43 @@ def main():
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         cold_ms = median_ms(attention, 5, before=lambda: flush.fill_(1))
         del flush
+    # the bucket-count sweep (2, 4, 6, 8 buckets) and the anchor-only baseline (l_p = 0) on
+    # the same context, each as one layer: score_select -> gather_passing -> attention
+    sweep = []
+    if not args.profile and w.keys == "frame" and w.frame_len > 0:
+        for lv in sweep_layouts(w):
+            L = apbv.Layout(lv["block_starts"], l_anchor=lv["l_anchor"], l_query=w.l_query,
+                            l_pass=lv["l_pass"], hq=w.hq, hkv=w.hkv, head_dim=w.head_dim,
+                            zigzag=True)
+            ws_v = torch.empty(max(apbv.score_select_workspace(L), 256), dtype=torch.uint8,
+                               device=dev)
+            sel_v = torch.empty((L.n_blocks, w.hkv, L.l_pass), dtype=torch.int32, device=dev)
+            kp_v = torch.empty((w.hkv, max(L.pre_rows, 1), w.head_dim), dtype=torch.bfloat16,
+                               device=dev)
+            vp_v = torch.empty_like(kp_v)
+
+            def select_gather(L=L, ws_v=ws_v, sel_v=sel_v, kp_v=kp_v, vp_v=vp_v):
+                apbv.score_select(L, d["q_query"], d["k_ctx"], sel=sel_v, workspace=ws_v,
+                                  want_scores=False)
+                apbv.gather_passing(L, d["k_anchor"], d["v_anchor"], d["k_ctx"], d["v_ctx"],
+                                    sel_v, k_pre=kp_v, v_pre=vp_v)
+
+            def attend_v(L=L, kp_v=kp_v, vp_v=vp_v):
+                apbv.approx_attn_prefill(L, d["q_ctx"], kp_v, vp_v, d["k_ctx"], d["v_ctx"],
+                                         out=out)
+
+            select_gather()
+            attend_v()
+            ms_sg = median_ms(select_gather, 3)
+            ms_at = median_ms(attend_v, 3)
+            fl = attention_flops(L.block_starts, L.l_anchor, L.l_pass, w.hq, w.head_dim)
+            sweep.append({"variant": lv["name"], "virtual_blocks": L.n_blocks,
+                          "buckets": apbv.num_buckets(L), "l_pass": L.l_pass,
+                          "layer_ms": ms_sg + ms_at, "attention_ms": ms_at,
+                          "tokens_per_s": x.N / ((ms_sg + ms_at) * 1e-3),
+                          "attention_tflops": fl / (ms_at * 1e-3) / 1e12,
+                          "attention_frac_of_peak": fl / (ms_at * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+            del ws_v, sel_v, kp_v, vp_v
     if args.calib_copy:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
         b = torch.empty_like(a)
@@ -277,6 +315,7 @@ def main():
         "query_forward_ms": q_ms,
         "layer_with_query_rows_tokens_per_s": (x.N + w.l_query) / ((ms_step + q_ms) * 1e-3),
         "gather_GBps": gather_bytes(lay, w.head_dim) / (float(per[:, 1].mean()) * 1e-3) / 1e9,
+        "sweep": sweep or None,
         "cpu_baseline": None,
     }
     if not (args.profile or args.no_cpu_baseline):

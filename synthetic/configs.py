@@ -91,3 +91,22 @@ def workload(name: str, **overrides) -> Workload:
     """Return a named workload, optionally with fields replaced (for scaled-down test cases)."""
     w = CONFIGS[name]
     return dataclasses.replace(w, **overrides) if overrides else w
+
+
+def sweep_layouts(w: Workload):
+    """Layouts of the bucket-count sweep and the no-passing baseline over the same context as
+    a fixed-frame workload (the pages evaluate 2, 4, 6 and 8 hosts, and name an anchor-only
+    method without passing blocks among the baselines). Each entry is a dict with ``name``,
+    ``block_starts`` (whole frames split evenly by count over 2H virtual blocks), ``l_anchor``
+    and ``l_pass``."""
+    from .gen import frame_partition
+    assert w.keys == "frame" and w.frame_len > 0 and w.total_tokens % w.frame_len == 0
+    frames = np.full(w.total_tokens // w.frame_len, w.frame_len, np.int64)
+    out = []
+    for h in (2, 4, 6, 8):
+        out.append(dict(name=f"buckets_{h}", block_starts=frame_partition(frames, 2 * h),
+                        l_anchor=w.l_anchor, l_pass=w.l_pass))
+    out.append(dict(name="no_passing", block_starts=frame_partition(frames, w.n_blocks),
+                    l_anchor=w.l_anchor, l_pass=0))
+    return out
+

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from synthetic import generate, workload
+from synthetic import generate, sweep_layouts, workload
 from gpu_util import (check_attention, check_selection, dev_bf16, host_f64, layout_of, say,
                       upload)
 import sequence_approximate_attention_score_amd as apbv
@@ -261,3 +261,19 @@ def test_dense_causal_128k_sampled():
                             f(k), f(v), [0, N], 0, 0, w.hq, w.hkv, 1 / math.sqrt(w.head_dim),
                             rows=rows, heads=[0, 27])
     check_attention(host_f64(out), o_or, "dense causal 128K")
+
+
+@pytest.mark.parametrize("name", ["buckets_2", "buckets_4", "buckets_6", "no_passing"])
+def test_sweep_128k_sampled(name):
+    """The bucket-count sweep (2, 4, 6 buckets over 128K tokens; 8 is the headline layout)
+    and the anchor-only baseline without passing blocks, on the same 128K context: sampled
+    blocks (scores, selection) and rows (attention, teacher-forced)."""
+    x = generate(workload("c2"))
+    lay_d = [l for l in sweep_layouts(x.w) if l["name"] == name][0]
+    lay = layout_of(x, block_starts=lay_d["block_starts"], l_anchor=lay_d["l_anchor"],
+                    l_pass=lay_d["l_pass"])
+    bs = lay_d["block_starts"]
+    rng = np.random.default_rng(11)
+    rows = sample_rows(bs, apbv.attn_tile_rows(x.w.head_dim), rng, per_block=12)
+    blocks = sorted({0, lay.n_blocks - 1})
+    full_check(x, lay, rows=rows, heads=[0, 13, 27], blocks=blocks)
