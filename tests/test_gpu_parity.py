@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from synthetic import generate, sweep_layouts, workload
+from synthetic import bf16_bits, generate, sweep_layouts, workload
 from gpu_util import (check_attention, check_selection, dev_bf16, host_f64, layout_of, say,
                       upload)
 import sequence_approximate_attention_score_amd as apbv
@@ -147,6 +147,8 @@ VARIANTS = {
                                list(range(0, 64 * 40 + 1, 40)), dict(zigzag=False)),
     "big_query_block": (dict(hq=4, hkv=2, head_dim=128, total_tokens=2500, l_anchor=100,
                              l_query=300, l_pass=64), [0, 1200, 2500], {}),
+    "d64_several_tiles": (dict(hq=8, hkv=2, head_dim=64, total_tokens=4096, l_anchor=128,
+                               l_query=32, l_pass=128), [0, 1024, 2048, 3072, 4096], {}),
 }
 
 
@@ -157,6 +159,17 @@ def test_variant(name):
                                      n_blocks=len(bs) - 1, **wkw), block_starts=bs)
     lay = layout_of(x, **lkw)
     full_check(x, lay)
+
+
+def test_running_max_rescales():
+    """Keys whose norm grows along the context push each row's running maximum up tile after
+    tile, so the lazy rescale of the running output and sum is taken many times."""
+    x = generate(dataclasses.replace(workload("c0"), name="grow", keys="iid", hq=4, hkv=2,
+                                     head_dim=128, total_tokens=2048, n_blocks=4, block_len=512,
+                                     l_anchor=64, l_query=16, l_pass=64))
+    f = (1.0 + 4.0 * np.arange(x.N) / x.N).astype(np.float32)
+    x.bits["k_ctx"] = bf16_bits(x.f32("k_ctx") * f[:, None, None])
+    full_check(x, layout_of(x))
 
 
 def test_single_block_is_dense_causal():
