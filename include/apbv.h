@@ -68,7 +68,8 @@ typedef struct apbv_layout {
   float scale;                 /* softmax scale; 0 means 1/sqrt(head_dim) */
   int32_t zigzag;              /* 1: ZigZag bucket schedule, 0: block order (same results) */
   int64_t q_row_stride;        /* elements between tokens of q_ctx; 0 means hq*head_dim */
-  int64_t kv_row_stride;       /* elements between tokens of k_ctx, v_ctx; 0 means hkv*head_dim */
+  int64_t kv_row_stride;       /* elements between tokens of k_ctx, v_ctx; 0 means hkv*head_dim;
+                                  below 2^22 */
 } apbv_layout;
 
 /* Workspace bytes needed by apbv_score_select for this layout (written to *bytes). */

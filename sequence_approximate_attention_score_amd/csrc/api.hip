@@ -74,6 +74,10 @@ apbv_status check_layout(const apbv_layout* L, Checked& c) {
   if (c.kv_stride < (int64_t)c.hkv * c.d || c.kv_stride % 8 != 0)
     return fail(APBV_EINVAL, "kv_row_stride = %lld must be >= hkv*head_dim and a multiple of 8",
                 (long long)c.kv_stride);
+  // tile loads address a K/V row with a 24-bit byte stride
+  if (c.kv_stride >= (int64_t)1 << 22)
+    return fail(APBV_EUNSUPPORTED, "kv_row_stride = %lld too large (limit 2^22 elements)",
+                (long long)c.kv_stride);
   if ((int64_t)c.G * c.l_q > 0x7fffffff / 2) return fail(APBV_EUNSUPPORTED, "too many score rows");
   return APBV_OK;
 }

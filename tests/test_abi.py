@@ -68,6 +68,7 @@ def call_attn(layout, **ptrs):
     (dict(scale=float("inf")), _lib.APBV_EINVAL),
     (dict(q_row_stride=100), _lib.APBV_EINVAL),                     # stride < hq*d
     (dict(kv_row_stride=260), _lib.APBV_EINVAL),                    # not a multiple of 8
+    (dict(kv_row_stride=1 << 22), _lib.APBV_EUNSUPPORTED),          # beyond the 24-bit stride
     (dict(block_starts=list(range(0, 66 * 8, 8))), _lib.APBV_EINVAL),  # > 64 blocks
 ])
 def test_invalid_layouts_are_rejected_before_launch(bad, code):
