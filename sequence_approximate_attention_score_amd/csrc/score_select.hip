@@ -32,7 +32,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void score_rowstats(const ScoreParams p) {
   constexpr int NK = D / 16;
   constexpr int KSTR = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kKeyTile * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKeyTile * KSTR];
 
   const int n_rg = (p.rows + 127) / 128;
   int b = blockIdx.x;
@@ -59,17 +59,33 @@ __global__ __launch_bounds__(kThreads) void score_rowstats(const ScoreParams p) 
       qf[ks] = as_bf16x8(ok ? load16(qrow + ks * 16) : u32x4{0, 0, 0, 0});
   }
 
-  float m = -INFINITY, l = 0.f;   // raw-logit max, sum of exp2((s - m) * c) over this lane's keys
-  for (int k0 = k_begin; k0 < k_end; k0 += kKeyTile) {
+  // K tiles: the next tile's rows are fetched into registers while the current one is
+  // computed, then stored into the other LDS stage (one barrier per tile)
+  constexpr int CPT = kKeyTile * D / 8 / kThreads;   // 16-byte chunks per thread per tile
+  u32x4 pre[CPT];
+  auto fetch = [&](int k0) {
     const int valid = min(kKeyTile, k_end - k0);
-    __syncthreads();
-    for (int c = threadIdx.x; c < kKeyTile * D / 8; c += kThreads) {
-      const int kr = c / (D / 8), col = c % (D / 8);
-      const u32x4 val = kr < valid ? load16(p.kc + (int64_t)(k0 + kr) * p.kv_stride + g * D + col * 8)
-                                   : u32x4{0, 0, 0, 0};
-      store16(sK + kr * KSTR + col * 8, val);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = threadIdx.x + c * kThreads;
+      const int kr = idx / (D / 8), col = idx % (D / 8);
+      pre[c] = kr < valid ? load16(p.kc + (int64_t)(k0 + kr) * p.kv_stride + g * D + col * 8)
+                          : u32x4{0, 0, 0, 0};
+    }
+  };
+  fetch(k_begin);
+  int buf = 0;
+  float m = -INFINITY, l = 0.f;   // raw-logit max, sum of exp2((s - m) * c) over this lane's keys
+  for (int k0 = k_begin; k0 < k_end; k0 += kKeyTile, buf ^= 1) {
+    const int valid = min(kKeyTile, k_end - k0);
+    uint16_t* sKb = sK + buf * kKeyTile * KSTR;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = threadIdx.x + c * kThreads;
+      store16(sKb + (idx / (D / 8)) * KSTR + (idx % (D / 8)) * 8, pre[c]);
     }
     __syncthreads();
+    if (k0 + kKeyTile < k_end) fetch(k0 + kKeyTile);
     f32x16 s[kKeyTile / 32];
 #pragma unroll
     for (int n = 0; n < kKeyTile / 32; ++n)
@@ -79,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void score_rowstats(const ScoreParams p) 
     for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
       for (int n = 0; n < kKeyTile / 32; ++n) {
-        const bf16x8 a = as_bf16x8(load16(sK + (n * 32 + l32) * KSTR + ks * 16 + half * 8));
+        const bf16x8 a = as_bf16x8(load16(sKb + (n * 32 + l32) * KSTR + ks * 16 + half * 8));
         s[n] = mfma32(a, qf[ks], s[n]);
       }
     float mx = -INFINITY;
@@ -115,8 +131,8 @@ __global__ __launch_bounds__(kThreads) void score_colsum(const ScoreParams p, in
   constexpr int NK = D / 16;
   constexpr int QSTR = D + 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem);                   // [kQChunk][QSTR]
-  float* sL = reinterpret_cast<float*>(smem + kQChunk * QSTR * 2);     // [rows_pad] lse2
+  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem);                   // [2][kQChunk][QSTR]
+  float* sL = reinterpret_cast<float*>(smem + 2 * kQChunk * QSTR * 2); // [rows_pad] lse2
 
   const int n_kt = (gridDim.x / (p.n_blocks * p.hkv));
   int b = blockIdx.x;
@@ -160,26 +176,42 @@ __global__ __launch_bounds__(kThreads) void score_colsum(const ScoreParams p, in
       kf[kg][ks] = as_bf16x8(ok ? load16(krow + ks * 16) : u32x4{0, 0, 0, 0});
   }
 
-  float col[2] = {0.f, 0.f};
-  for (int c0 = 0; c0 < p.rows; c0 += kQChunk) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < kQChunk * D / 8; c += kThreads) {
-      const int qr = c / (D / 8), cc = c % (D / 8);
-      const int r = c0 + qr;
+  // query-row chunks: the next chunk is fetched into registers while the current one is
+  // used, then stored into the other LDS stage (one barrier per chunk)
+  constexpr int CPT = kQChunk * D / 8 / kThreads;   // 16-byte chunks per thread per chunk
+  u32x4 pre[CPT];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = threadIdx.x + c * kThreads;
+      const int r = c0 + idx / (D / 8), cc = idx % (D / 8);
       u32x4 val = {0, 0, 0, 0};
       if (r < p.rows) {
         const int h = g * p.group + r / p.l_query, qi = r % p.l_query;
         val = load16(p.qq + ((int64_t)qi * p.hq + h) * D + cc * 8);
       }
-      store16(sQ + qr * QSTR + cc * 8, val);
+      pre[c] = val;
+    }
+  };
+  fetch(0);
+  __syncthreads();   // the row statistics in sL are complete
+  float col[2] = {0.f, 0.f};
+  int buf = 0;
+  for (int c0 = 0; c0 < p.rows; c0 += kQChunk, buf ^= 1) {
+    uint16_t* sQb = sQ + buf * kQChunk * QSTR;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = threadIdx.x + c * kThreads;
+      store16(sQb + (idx / (D / 8)) * QSTR + (idx % (D / 8)) * 8, pre[c]);
     }
     __syncthreads();
+    if (c0 + kQChunk < p.rows) fetch(c0 + kQChunk);
     const int nrb = min(kQChunk, p.rows - c0 + 31) / 32;
     for (int rb = 0; rb < nrb; ++rb) {
       bf16x8 af[NK];
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks)
-        af[ks] = as_bf16x8(load16(sQ + (rb * 32 + l32) * QSTR + ks * 16 + half * 8));
+        af[ks] = as_bf16x8(load16(sQb + (rb * 32 + l32) * QSTR + ks * 16 + half * 8));
       const int rbase = c0 + rb * 32 + 4 * half;
       float lse[16];
 #pragma unroll
@@ -308,7 +340,8 @@ hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block
   {
     const int n_kt = (max_block + kColKeys - 1) / kColKeys;
     const int rows_pad = ((p.rows + kQChunk - 1) / kQChunk) * kQChunk;
-    const size_t shm = (size_t)kQChunk * (head_dim + 8) * 2 + (size_t)(rows_pad > 0 ? rows_pad : 1) * 4;
+    const size_t shm = 2 * (size_t)kQChunk * (head_dim + 8) * 2 +
+                       (size_t)(rows_pad > 0 ? rows_pad : 1) * 4;
     dim3 grid(p.n_blocks * p.hkv * n_kt);
     if (head_dim == 128)
       hipLaunchKernelGGL(score_colsum<128>, grid, dim3(kThreads), shm, stream, p, rows_pad);
