@@ -290,3 +290,46 @@ def test_sweep_128k_sampled(name):
     rows = sample_rows(bs, apbv.attn_tile_rows(x.w.head_dim), rng, per_block=12)
     blocks = sorted({0, lay.n_blocks - 1})
     full_check(x, lay, rows=rows, heads=[0, 13, 27], blocks=blocks)
+
+
+def _guarded(shape, dtype, fill):
+    """A tensor view with 4096 guard elements before and after it, all set to ``fill``."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 8192,), fill, dtype=dtype, device="cuda")
+    return buf, buf[4096:4096 + n].view(shape)
+
+
+def test_outputs_stay_in_bounds():
+    """Every call writes only its own outputs: guard regions around scores, selection, the
+    prefix, the attention output and lse, and the query rows' output keep their fill."""
+    x = generate(dataclasses.replace(workload("c0"), name="guard", keys="iid", hq=14, hkv=2,
+                                     head_dim=128, total_tokens=1000, n_blocks=5, block_len=0,
+                                     l_anchor=37, l_query=19, l_pass=21),
+                 block_starts=[0, 129, 300, 555, 700, 1000])
+    lay = layout_of(x)
+    d = upload(x, ("q_query", "q_ctx", "k_ctx", "v_ctx", "k_anchor", "v_anchor", "k_query",
+                   "v_query"))
+    w = x.w
+    bufs = {}
+    bufs["scores"] = _guarded((w.hkv, x.N), torch.float32, 7.0)
+    bufs["sel"] = _guarded((lay.n_blocks, w.hkv, lay.l_pass), torch.int32, -7)
+    bufs["k_pre"] = _guarded((w.hkv, lay.pre_rows, w.head_dim), torch.bfloat16, 7.0)
+    bufs["v_pre"] = _guarded((w.hkv, lay.pre_rows, w.head_dim), torch.bfloat16, 7.0)
+    bufs["out"] = _guarded((x.N, w.hq, w.head_dim), torch.bfloat16, 7.0)
+    bufs["lse"] = _guarded((w.hq, x.N), torch.float32, 7.0)
+    bufs["q_out"] = _guarded((w.l_query, w.hq, w.head_dim), torch.bfloat16, 7.0)
+    bufs["q_lse"] = _guarded((w.hq, w.l_query), torch.float32, 7.0)
+    v = {k: b[1] for k, b in bufs.items()}
+    apbv.score_select(lay, d["q_query"], d["k_ctx"], scores=v["scores"], sel=v["sel"])
+    apbv.gather_passing(lay, d["k_anchor"], d["v_anchor"], d["k_ctx"], d["v_ctx"], v["sel"],
+                        k_pre=v["k_pre"], v_pre=v["v_pre"])
+    apbv.approx_attn_prefill(lay, d["q_ctx"], v["k_pre"], v["v_pre"], d["k_ctx"], d["v_ctx"],
+                             out=v["out"], lse=v["lse"])
+    apbv.query_forward(lay, d["q_query"], d["k_query"], d["v_query"], d["k_anchor"],
+                       d["v_anchor"], d["k_ctx"], d["v_ctx"], out=v["q_out"], lse=v["q_lse"])
+    torch.cuda.synchronize()
+    for name, (buf, view) in bufs.items():
+        fill = buf[0].item()
+        assert torch.all(buf[:4096] == fill) and torch.all(buf[-4096:] == fill), name
+        assert torch.isfinite(view.float()).all() or name == "sel", name
+    say("  guards intact around every output")
