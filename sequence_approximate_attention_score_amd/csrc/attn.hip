@@ -97,7 +97,8 @@ struct Loader {
   }
   // One tile (K or V rows from `base`, row stride `stride` elements, `valid` rows) into
   // `dst`. Rows past `valid` repeat the last valid row (masked later, only need to be
-  // finite). Byte offsets are 24-bit products: a tile spans at most 64 rows of < 2^17 bytes.
+  // finite). Byte offsets are 24-bit products: a row index below 64 times a row stride
+  // below 2^23 bytes (the C ABI rejects larger K/V strides).
   template <int SEGS>
   __device__ __forceinline__ void load(uint16_t* dst, const uint16_t* base, int64_t stride,
                                        int valid) const {
@@ -275,8 +276,9 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, 
   const int n_pre = (P + kKT - 1) / kKT;
   const int n_loc = (r1 - lo + kKT - 1) / kKT;
   const int ntiles = n_pre + n_loc;
-  // tiles this wave computes: every prefix tile, and local tiles up to its last row
-  const int n_live = n_pre + min(n_loc, (wrow0 + 31 - lo) / kKT + 1);
+  // tiles this wave computes: every prefix tile, and local tiles up to its last row; a wave
+  // whose rows all lie past the end of a short last tile computes nothing
+  const int n_live = wrow0 >= r1 ? 0 : n_pre + min(n_loc, (wrow0 + 31 - lo) / kKT + 1);
 
   auto source = [&](int i) -> KeySrc {
     KeySrc s;
