@@ -150,8 +150,8 @@ apbv_status apbv_query_forward_workspace(const apbv_layout* layout, size_t* byte
  *   k_anchor[:, g]  ++  k_ctx[0 .. N-1, g]  ++  k_query[0 .. i, g]
  *   out[i, h, :] = softmax(scale * q_query[i,h] . keys) @ values       (bf16, round-to-nearest)
  *   lse[h, i]    = natural-log log-sum-exp of the scaled logits         (fp32, optional)
- * computed as partial results over chunks of at most 4096 keys (bf16 MFMA, fp32 softmax),
- * merged in a second kernel.
+ * computed as partial results over chunks of 1024-8192 keys (bf16 MFMA, fp32 softmax; the
+ * chunk length depends only on the layout), merged in a second kernel.
  *
  *   q_query          [l_query, hq, d] bf16, contiguous
  *   k_query, v_query [l_query, hkv, d] bf16, contiguous

@@ -82,7 +82,7 @@ hipError_t launch_attention(const AttnParams& p, int head_dim, hipStream_t strea
 
 // ---------------------------------------------------------------- query-block rows
 // Keys of the query rows = [anchor | context | query block (causal)], cut into chunks of
-// kQueryChunk keys that never straddle two sources; chunk c of the grid computes the
+// chunk_keys keys that never straddle two sources; chunk c of the grid computes the
 // normalised partial output and lse of every query row over its keys, and the merge
 // combines the chunks of a row through their lse.
 struct QueryParams {
@@ -99,13 +99,12 @@ struct QueryParams {
   float* lse;           // [hq, l_q] or null
   int64_t kv_stride;
   int32_t hq, hkv, group, l_query, l_anchor, n_tokens;
-  int32_t n_anchor_chunks, n_ctx_chunks, n_query_chunks, n_chunks, row_tiles;
+  int32_t chunk_keys, n_anchor_chunks, n_ctx_chunks, n_query_chunks, n_chunks, row_tiles;
   float scale_log2;
 };
 
-constexpr int kQueryChunk = 4096;   // keys per partial (a multiple of the 64-key tile)
-
 struct QueryPlan {
+  int chunk_keys;   // keys per partial, a multiple of the 64-key tile
   int n_anchor_chunks, n_ctx_chunks, n_query_chunks, n_chunks, row_tiles;
   size_t o_bytes, lse_bytes;   // workspace parts, each rounded up to 256 bytes
 };

@@ -375,6 +375,7 @@ apbv_status apbv_query_forward(const apbv_layout* layout, const apbv_bf16* q_que
   p.l_query = c.l_q;
   p.l_anchor = c.l_a;
   p.n_tokens = c.N;
+  p.chunk_keys = q.chunk_keys;
   p.n_anchor_chunks = q.n_anchor_chunks;
   p.n_ctx_chunks = q.n_ctx_chunks;
   p.n_query_chunks = q.n_query_chunks;

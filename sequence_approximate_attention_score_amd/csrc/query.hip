@@ -6,8 +6,9 @@
 // block's keys 0..i.
 //
 // Two kernels:
-//  1. query_partial_kernel: one workgroup = 8 waves x 32 rows over one chunk of at most
-//     kQueryChunk keys of one KV head. The rows are the G heads of the KV group times the
+//  1. query_partial_kernel: one workgroup = 8 waves x 32 rows over one chunk of keys of
+//     one KV head (the chunk length is chosen so that the grid fills whole rounds of the
+//     256 compute units). The rows are the G heads of the KV group times the
 //     l_q query rows, packed into the MFMA row dimension, so each K/V tile staged in LDS
 //     serves the whole group. It writes the chunk's normalised fp32 output and lse.
 //  2. query_merge_kernel: one wave per (head, row) folds the chunks through their lse and
@@ -54,20 +55,20 @@ __global__ __launch_bounds__(kWaves * 64) void query_partial_kernel(const QueryP
   int len, kpos0;
   bool causal = false;
   if (c < p.n_anchor_chunks) {
-    kpos0 = c * kQueryChunk;
-    len = min(kQueryChunk, p.l_anchor - kpos0);
+    kpos0 = c * p.chunk_keys;
+    len = min(p.chunk_keys, p.l_anchor - kpos0);
     stride = (int64_t)p.hkv * D;
     kb = p.ka + (int64_t)kpos0 * stride + g * D;
     vb = p.va + (int64_t)kpos0 * stride + g * D;
   } else if (c < p.n_anchor_chunks + p.n_ctx_chunks) {
-    kpos0 = (c - p.n_anchor_chunks) * kQueryChunk;
-    len = min(kQueryChunk, p.n_tokens - kpos0);
+    kpos0 = (c - p.n_anchor_chunks) * p.chunk_keys;
+    len = min(p.chunk_keys, p.n_tokens - kpos0);
     stride = p.kv_stride;
     kb = p.kc + (int64_t)kpos0 * stride + g * D;
     vb = p.vc + (int64_t)kpos0 * stride + g * D;
   } else {
-    kpos0 = (c - p.n_anchor_chunks - p.n_ctx_chunks) * kQueryChunk;
-    len = min(kQueryChunk, p.l_query - kpos0);
+    kpos0 = (c - p.n_anchor_chunks - p.n_ctx_chunks) * p.chunk_keys;
+    len = min(p.chunk_keys, p.l_query - kpos0);
     stride = (int64_t)p.hkv * D;
     kb = p.kq + (int64_t)kpos0 * stride + g * D;
     vb = p.vq + (int64_t)kpos0 * stride + g * D;
@@ -198,12 +199,31 @@ __global__ __launch_bounds__(256) void query_merge_kernel(const QueryParams p) {
 
 QueryPlan plan_query(int l_anchor, int n_tokens, int l_query, int hq, int hkv, int head_dim) {
   QueryPlan q;
-  q.n_anchor_chunks = (l_anchor + kQueryChunk - 1) / kQueryChunk;
-  q.n_ctx_chunks = (n_tokens + kQueryChunk - 1) / kQueryChunk;
-  q.n_query_chunks = (l_query + kQueryChunk - 1) / kQueryChunk;
-  q.n_chunks = q.n_anchor_chunks + q.n_ctx_chunks + q.n_query_chunks;
   const int64_t rows = (int64_t)(hq / hkv) * l_query;
   q.row_tiles = (int)((rows + kRows - 1) / kRows);
+  // chunk length: among multiples of 64 keys from 1024 to 8192, the one whose grid wastes
+  // the least of its last round on 256 compute units (the largest such chunk on ties, for
+  // fewer partials), preferring grids of at least two rounds
+  auto chunks_of = [&](int ck) {
+    return (l_anchor + ck - 1) / ck + (n_tokens + ck - 1) / ck + (l_query + ck - 1) / ck;
+  };
+  constexpr int kCUs = 256;
+  int best = 8192;
+  double best_eff = -1.0;
+  for (int ck = 8192; ck >= 1024; ck -= 64) {
+    const int64_t wgs = (int64_t)q.row_tiles * hkv * chunks_of(ck);
+    const int64_t rounds = (wgs + kCUs - 1) / kCUs;
+    const double eff = (double)wgs / (double)(rounds * kCUs) - (rounds < 2 ? 1.0 : 0.0);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = ck;
+    }
+  }
+  q.chunk_keys = best;
+  q.n_anchor_chunks = (l_anchor + best - 1) / best;
+  q.n_ctx_chunks = (n_tokens + best - 1) / best;
+  q.n_query_chunks = (l_query + best - 1) / best;
+  q.n_chunks = q.n_anchor_chunks + q.n_ctx_chunks + q.n_query_chunks;
   const size_t prow = (size_t)q.n_chunks * hq * l_query;
   q.o_bytes = (prow * head_dim * sizeof(float) + 255) & ~(size_t)255;
   q.lse_bytes = (prow * sizeof(float) + 255) & ~(size_t)255;

@@ -117,7 +117,7 @@ def test_query_forward_validation():
     L = apbv.lib()
     n = ctypes.c_size_t(0)
     assert L.apbv_query_forward_workspace(lay.ref(), ctypes.byref(n)) == 0
-    # chunks: 1 anchor + 1 context (<= 4096 keys each) + 1 query; fp32 outputs and lse
+    # chunks: 1 anchor + 1 context + 1 query (small layouts take one chunk per source)
     chunks = 3
     o_bytes = -(-chunks * 4 * 32 * 128 * 4 // 256) * 256
     lse_bytes = -(-chunks * 4 * 32 * 4 // 256) * 256
