@@ -129,6 +129,9 @@ constexpr int kScoreSplit = 2048;   // keys per row-statistics workgroup
 
 size_t score_workspace_bytes(int n_blocks, int hkv, int rows, int n_split, int n_tokens,
                              bool need_scores);
+// LDS of one column-sum workgroup (two staged query chunks and the rows' log-sum-exps)
+size_t score_colsum_lds_bytes(int rows, int head_dim);
+constexpr size_t kMaxLdsBytes = 160 * 1024;   // per workgroup on gfx950
 hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block,
                                hipStream_t stream);
 

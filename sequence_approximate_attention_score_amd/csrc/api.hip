@@ -167,6 +167,8 @@ apbv_status apbv_score_select(const apbv_layout* layout, const apbv_bf16* q_quer
   if (scores != nullptr && ((uintptr_t)scores & 3u) != 0)
     return fail(APBV_EINVAL, "scores is not 4-byte aligned");
   const int rows = c.G * c.l_q;
+  if (score_colsum_lds_bytes(rows, c.d) > kMaxLdsBytes)
+    return fail(APBV_EUNSUPPORTED, "G * l_query = %d score rows exceed the column-sum LDS", rows);
   const int n_split = n_split_of(c);
   const size_t need = score_workspace_bytes(c.n, c.hkv, rows, n_split, c.N, scores == nullptr);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))

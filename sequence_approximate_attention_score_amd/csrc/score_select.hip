@@ -325,6 +325,11 @@ size_t score_workspace_bytes(int n_blocks, int hkv, int rows, int n_split, int n
   return stats + sc;
 }
 
+size_t score_colsum_lds_bytes(int rows, int head_dim) {
+  const int rows_pad = ((rows + kQChunk - 1) / kQChunk) * kQChunk;
+  return 2 * (size_t)kQChunk * (head_dim + 8) * 2 + (size_t)(rows_pad > 0 ? rows_pad : 1) * 4;
+}
+
 hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block,
                                hipStream_t stream) {
   const int n_rg = (p.rows + 127) / 128;
@@ -340,8 +345,7 @@ hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block
   {
     const int n_kt = (max_block + kColKeys - 1) / kColKeys;
     const int rows_pad = ((p.rows + kQChunk - 1) / kQChunk) * kQChunk;
-    const size_t shm = 2 * (size_t)kQChunk * (head_dim + 8) * 2 +
-                       (size_t)(rows_pad > 0 ? rows_pad : 1) * 4;
+    const size_t shm = score_colsum_lds_bytes(p.rows, head_dim);
     dim3 grid(p.n_blocks * p.hkv * n_kt);
     if (head_dim == 128)
       hipLaunchKernelGGL(score_colsum<128>, grid, dim3(kThreads), shm, stream, p, rows_pad);
