@@ -249,7 +249,7 @@ __device__ __forceinline__ void process_tile(const AttnParams& p, int h, int g, 
                                              uint16_t* K0, uint16_t* K1, uint16_t* V0,
                                              uint16_t* V1, const Loader<D>& ld) {
   using G = Geo<D>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int lo = p.sched.bs[v], hi = p.sched.bs[v + 1];
   const int r0 = lo + t * kRows;
