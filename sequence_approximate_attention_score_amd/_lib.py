@@ -1,8 +1,9 @@
 """ctypes binding of ``libapbv.so`` (argument marshalling only).
 
-Every step of the hot path runs in the library's HIP kernels; this module converts torch
-tensors into device pointers, allocates outputs the caller did not provide (torch is the
-device-memory and stream plumbing) and raises ``ApbvError`` on a non-zero status.
+Every step of the hot path runs in the library's HIP kernels; this module checks that torch
+tensors have the dtype, shape and strides the C ABI assumes, converts them into device
+pointers, allocates outputs the caller did not provide (torch is the device-memory and
+stream plumbing) and raises ``ApbvError`` on a non-zero status.
 Importing it fails loudly when the library has not been built.
 """
 from __future__ import annotations
@@ -92,6 +93,8 @@ class Layout:
         self.hq, self.hkv, self.head_dim = int(hq), int(hkv), int(head_dim)
         self.n_tokens = int(bs[-1]) if bs.size else 0
         self.pre_rows = self.l_anchor + self.n_blocks * self.l_pass
+        self.q_stride = int(q_row_stride) or self.hq * self.head_dim
+        self.kv_stride = int(kv_row_stride) or self.hkv * self.head_dim
         self.c = _Layout(self.n_blocks, bs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                          self.l_anchor, self.l_query, self.l_pass, self.hq, self.hkv,
                          self.head_dim, float(scale), int(bool(zigzag)), int(q_row_stride),
@@ -103,6 +106,51 @@ class Layout:
 
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
+
+
+def _arg(t, name: str, dtype, rows: int, row_elems: int, row_stride: int | None = None,
+         required: bool = True):
+    """Check tensor argument ``name`` against what the C ABI assumes: ``dtype``, ``rows`` rows
+    of ``row_elems`` contiguous elements, rows ``row_stride`` elements apart (default: packed).
+    Returns (name, tensor or None); ``_pointers`` checks the device and takes the addresses."""
+    import torch
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required for this layout")
+        return name, None
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    stride = row_elems if row_stride is None else row_stride
+    inner = int(np.prod(t.shape[1:])) if t.dim() > 1 else (1 if t.dim() == 1 else 0)
+    if t.dim() < 1 or t.shape[0] != rows or inner != row_elems:
+        raise ValueError(f"{name} must hold {rows} rows of {row_elems} elements, got shape "
+                         f"{tuple(t.shape)}")
+    if rows > 0 and row_elems > 0:
+        ok = rows == 1 or t.stride(0) == stride
+        step = 1
+        for dim in range(t.dim() - 1, 0, -1):       # inner dims packed (size-1 dims: any stride)
+            ok = ok and (t.shape[dim] == 1 or t.stride(dim) == step)
+            step *= int(t.shape[dim])
+        if not ok:
+            raise ValueError(f"{name} rows must be contiguous and {stride} elements apart, "
+                             f"got strides {tuple(t.stride())}")
+    return name, t
+
+
+def _pointers(*args):
+    """Device addresses of checked arguments; all tensors must sit on one CUDA device."""
+    dev = None
+    for name, t in args:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA tensor")
+        if dev is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other arguments on {dev}")
+        dev = t.device
+    return tuple(None if t is None else t.data_ptr() for _, t in args)
 
 
 def _stream(device) -> int:
@@ -151,8 +199,15 @@ def score_select(layout: Layout, q_query, k_ctx, *, scores=None, sel=None, works
         sel = torch.empty((layout.n_blocks, layout.hkv, layout.l_pass), dtype=torch.int32, device=dev)
     if workspace is None:
         workspace = torch.empty(max(score_select_workspace(layout), 256), dtype=torch.uint8, device=dev)
-    _check(lib().apbv_score_select(layout.ref(), _ptr(q_query), _ptr(k_ctx), _ptr(scores),
-                                   _ptr(sel), _ptr(workspace), workspace.numel(), _stream(dev)),
+    L, d = layout, layout.head_dim
+    bf, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    args = _pointers(
+        _arg(q_query, "q_query", bf, L.l_query, L.hq * d, required=L.l_query > 0),
+        _arg(k_ctx, "k_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(scores, "scores", f32, L.hkv, L.n_tokens, required=False),
+        _arg(sel, "sel", i32, L.n_blocks, L.hkv * L.l_pass),
+        _arg(workspace, "workspace", torch.uint8, workspace.numel(), 1))
+    _check(lib().apbv_score_select(L.ref(), *args, workspace.numel(), _stream(dev)),
            "apbv_score_select")
     return scores, sel
 
@@ -166,9 +221,18 @@ def gather_passing(layout: Layout, k_anchor, v_anchor, k_ctx, v_ctx, sel, *, k_p
         k_pre = torch.empty(shape, dtype=torch.bfloat16, device=k_ctx.device)
     if v_pre is None:
         v_pre = torch.empty(shape, dtype=torch.bfloat16, device=k_ctx.device)
-    _check(lib().apbv_gather_passing(layout.ref(), _ptr(k_anchor), _ptr(v_anchor), _ptr(k_ctx),
-                                     _ptr(v_ctx), _ptr(sel), _ptr(k_pre), _ptr(v_pre),
-                                     _stream(k_ctx.device)), "apbv_gather_passing")
+    L, d, bf = layout, layout.head_dim, torch.bfloat16
+    has_anchor = L.l_anchor > 0
+    args = _pointers(
+        _arg(k_anchor, "k_anchor", bf, L.l_anchor, L.hkv * d, required=has_anchor),
+        _arg(v_anchor, "v_anchor", bf, L.l_anchor, L.hkv * d, required=has_anchor),
+        _arg(k_ctx, "k_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(v_ctx, "v_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(sel, "sel", torch.int32, L.n_blocks, L.hkv * L.l_pass),
+        _arg(k_pre, "k_pre", bf, L.hkv, L.pre_rows * d),
+        _arg(v_pre, "v_pre", bf, L.hkv, L.pre_rows * d))
+    _check(lib().apbv_gather_passing(L.ref(), *args, _stream(k_ctx.device)),
+           "apbv_gather_passing")
     return k_pre, v_pre
 
 
@@ -181,10 +245,18 @@ def approx_attn_prefill(layout: Layout, q_ctx, k_pre, v_pre, k_ctx, v_ctx, *, ou
                           device=q_ctx.device)
     if want_lse and lse is None:
         lse = torch.empty((layout.hq, layout.n_tokens), dtype=torch.float32, device=q_ctx.device)
-    _check(lib().apbv_approx_attn_prefill(layout.ref(), _ptr(q_ctx), _ptr(k_pre), _ptr(v_pre),
-                                          _ptr(k_ctx), _ptr(v_ctx), _ptr(out), _ptr(lse),
-                                          range_begin, range_end, _stream(q_ctx.device)),
-           "apbv_approx_attn_prefill")
+    L, d, bf = layout, layout.head_dim, torch.bfloat16
+    has_pre = L.pre_rows > 0
+    args = _pointers(
+        _arg(q_ctx, "q_ctx", bf, L.n_tokens, L.hq * d, L.q_stride),
+        _arg(k_pre, "k_pre", bf, L.hkv, L.pre_rows * d, required=has_pre),
+        _arg(v_pre, "v_pre", bf, L.hkv, L.pre_rows * d, required=has_pre),
+        _arg(k_ctx, "k_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(v_ctx, "v_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(out, "out", bf, L.n_tokens, L.hq * d),
+        _arg(lse, "lse", torch.float32, L.hq, L.n_tokens, required=False))
+    _check(lib().apbv_approx_attn_prefill(L.ref(), *args, range_begin, range_end,
+                                          _stream(q_ctx.device)), "apbv_approx_attn_prefill")
     return out, lse
 
 
@@ -209,10 +281,21 @@ def query_forward(layout: Layout, q_query, k_query, v_query, k_anchor, v_anchor,
     if workspace is None:
         workspace = torch.empty(max(query_forward_workspace(layout), 256), dtype=torch.uint8,
                                 device=dev)
-    _check(lib().apbv_query_forward(layout.ref(), _ptr(q_query), _ptr(k_query), _ptr(v_query),
-                                    _ptr(k_anchor), _ptr(v_anchor), _ptr(k_ctx), _ptr(v_ctx),
-                                    _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-                                    _stream(dev)), "apbv_query_forward")
+    L, d, bf = layout, layout.head_dim, torch.bfloat16
+    any_q, has_anchor = L.l_query > 0, L.l_anchor > 0
+    args = _pointers(
+        _arg(q_query, "q_query", bf, L.l_query, L.hq * d, required=any_q),
+        _arg(k_query, "k_query", bf, L.l_query, L.hkv * d, required=any_q),
+        _arg(v_query, "v_query", bf, L.l_query, L.hkv * d, required=any_q),
+        _arg(k_anchor, "k_anchor", bf, L.l_anchor, L.hkv * d, required=has_anchor),
+        _arg(v_anchor, "v_anchor", bf, L.l_anchor, L.hkv * d, required=has_anchor),
+        _arg(k_ctx, "k_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(v_ctx, "v_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(out, "out", bf, L.l_query, L.hq * d),
+        _arg(lse, "lse", torch.float32, L.hq, L.l_query, required=False),
+        _arg(workspace, "workspace", torch.uint8, workspace.numel(), 1))
+    _check(lib().apbv_query_forward(L.ref(), *args, workspace.numel(), _stream(dev)),
+           "apbv_query_forward")
     return out, lse
 
 

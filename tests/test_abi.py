@@ -40,16 +40,6 @@ def small_layout(**kw):
     return apbv.Layout(args.pop("block_starts"), **args)
 
 
-class FakePtr:
-    """Stands in for a tensor: only data_ptr() is used by the binding's validation path."""
-
-    def __init__(self, addr):
-        self.addr = addr
-
-    def data_ptr(self):
-        return self.addr
-
-
 def call_attn(layout, **ptrs):
     p = dict(q=0x1000, kp=0x2000, vp=0x3000, kc=0x4000, vc=0x5000, out=0x6000, lse=None)
     p.update(ptrs)
@@ -222,3 +212,81 @@ def test_schedule_ranges_partition_the_units():
     full = apbv.schedule(lay)
     parts = np.concatenate([apbv.schedule(lay, b, b + 1) for b in range(nb)])
     assert np.array_equal(full, parts)
+
+
+def cpu_inputs(lay, fused_stride=None):
+    """Host tensors shaped as the binding expects (the checks run before any device use)."""
+    import torch
+    N, d, bf = lay.n_tokens, lay.head_dim, torch.bfloat16
+    t = dict(q_query=torch.zeros(lay.l_query, lay.hq, d, dtype=bf),
+             q_ctx=torch.zeros(N, lay.hq, d, dtype=bf),
+             k_ctx=torch.zeros(N, lay.hkv, d, dtype=bf), v_ctx=torch.zeros(N, lay.hkv, d, dtype=bf),
+             k_anchor=torch.zeros(lay.l_anchor, lay.hkv, d, dtype=bf),
+             v_anchor=torch.zeros(lay.l_anchor, lay.hkv, d, dtype=bf),
+             sel=torch.zeros(lay.n_blocks, lay.hkv, lay.l_pass, dtype=torch.int32),
+             k_pre=torch.zeros(lay.hkv, lay.pre_rows, d, dtype=bf),
+             v_pre=torch.zeros(lay.hkv, lay.pre_rows, d, dtype=bf))
+    if fused_stride:
+        F = torch.zeros(N, fused_stride, dtype=bf)
+        qd, kd = lay.hq * d, lay.hkv * d
+        t.update(q_ctx=F[:, :qd], k_ctx=F[:, qd:qd + kd], v_ctx=F[:, qd + kd:qd + 2 * kd])
+    return t
+
+
+def test_binding_rejects_wrong_tensors_before_launch():
+    import torch
+    lay = small_layout()
+    t = cpu_inputs(lay)
+
+    def err(fn):
+        with pytest.raises(ValueError) as e:
+            fn()
+        return str(e.value)
+
+    # every check but the device one passes: host tensors are refused last
+    assert "CUDA" in err(lambda: apbv.score_select(lay, t["q_query"], t["k_ctx"]))
+    assert "CUDA" in err(lambda: apbv.gather_passing(lay, t["k_anchor"], t["v_anchor"], t["k_ctx"],
+                                                     t["v_ctx"], t["sel"]))
+    assert "CUDA" in err(lambda: apbv.approx_attn_prefill(lay, t["q_ctx"], t["k_pre"], t["v_pre"],
+                                                          t["k_ctx"], t["v_ctx"], want_lse=True))
+    # dtype
+    assert "bfloat16" in err(lambda: apbv.score_select(lay, t["q_query"].float(), t["k_ctx"]))
+    assert "int32" in err(lambda: apbv.gather_passing(lay, t["k_anchor"], t["v_anchor"], t["k_ctx"],
+                                                      t["v_ctx"], t["sel"].long()))
+    assert "float32" in err(lambda: apbv.approx_attn_prefill(
+        lay, t["q_ctx"], t["k_pre"], t["v_pre"], t["k_ctx"], t["v_ctx"],
+        lse=torch.zeros(lay.hq, lay.n_tokens, dtype=torch.float64)))
+    # shape: rows and row length
+    assert "rows" in err(lambda: apbv.score_select(lay, t["q_query"], t["k_ctx"][:-1]))
+    assert "rows" in err(lambda: apbv.approx_attn_prefill(
+        lay, t["q_ctx"], t["k_pre"][:, :-1], t["v_pre"], t["k_ctx"], t["v_ctx"]))
+    assert "rows" in err(lambda: apbv.approx_attn_prefill(
+        lay, t["q_ctx"], t["k_pre"], t["v_pre"], t["k_ctx"], t["v_ctx"],
+        lse=torch.zeros(lay.n_tokens, lay.hq)))                  # transposed lse
+    # strides: a packed layout refuses a row-strided view; inner dims must be packed
+    wide = torch.zeros(lay.n_tokens, 2 * lay.hkv, lay.head_dim, dtype=torch.bfloat16)
+    assert "apart" in err(lambda: apbv.score_select(lay, t["q_query"], wide[:, :lay.hkv]))
+    assert "apart" in err(lambda: apbv.gather_passing(
+        lay, t["k_anchor"], t["v_anchor"], t["k_ctx"], t["v_ctx"],
+        t["sel"].transpose(1, 2).contiguous().transpose(1, 2)))
+    # a required operand missing (the layout has an anchor)
+    assert "required" in err(lambda: apbv.gather_passing(lay, None, t["v_anchor"], t["k_ctx"],
+                                                         t["v_ctx"], t["sel"]))
+    assert "required" in err(lambda: apbv.query_forward(lay, t["q_query"], None, None,
+                                                        t["k_anchor"], t["v_anchor"], t["k_ctx"],
+                                                        t["v_ctx"]))
+
+
+def test_binding_accepts_row_strided_views_of_a_fused_projection():
+    hq, hkv, d = 4, 2, 128
+    stride = (hq + 2 * hkv) * d
+    lay = small_layout(q_row_stride=stride, kv_row_stride=stride)
+    t = cpu_inputs(lay, fused_stride=stride)
+    for fn in (lambda: apbv.score_select(lay, t["q_query"], t["k_ctx"]),
+               lambda: apbv.approx_attn_prefill(lay, t["q_ctx"], t["k_pre"], t["v_pre"],
+                                                t["k_ctx"], t["v_ctx"])):
+        with pytest.raises(ValueError, match="CUDA"):            # only the device check is left
+            fn()
+    packed = cpu_inputs(small_layout())                          # packed k_ctx, strided layout
+    with pytest.raises(ValueError, match="apart"):
+        apbv.score_select(lay, t["q_query"], packed["k_ctx"])
