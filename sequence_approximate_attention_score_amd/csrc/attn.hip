@@ -53,8 +53,10 @@ constexpr int kRows = kWaves * 32;    // query rows per work tile
 constexpr int kNoCausal = 1 << 30;    // position of a row that no causal source limits
 constexpr float kTau = 8.0f;          // log2 headroom before the running offset is raised
 
-// sched_group_barrier classes
-constexpr int kSchedVALU = 0x2, kSchedMFMA = 0x8, kSchedDSRead = 0x100;
+// sched_group_barrier classes. Transcendental ops (v_exp_f32) are a class of their own
+// (0x400) that the plain vector class does not take, so the softmax groups name both.
+constexpr int kSchedVALU = 0x2, kSchedMFMA = 0x8, kSchedDSRead = 0x100, kSchedTrans = 0x400;
+constexpr int kSchedVector = kSchedVALU | kSchedTrans;
 
 template <int D>
 struct Geo {
@@ -226,21 +228,22 @@ __device__ __forceinline__ void pipe_step(const uint16_t* kbuf, const uint16_t* 
   l_run += ls;
   mx = row_max(sn);
 
-  // instruction order: phase A = per S MFMA one K read (two ahead) and 5 vector ops,
-  // phase B = per PV MFMA two transposing reads (four ahead) and 3 vector ops
+  // instruction order: phase A = per S MFMA one K read (two ahead) and 5 vector ops (the 32
+  // exponentials included, two or three behind each MFMA), phase B = per PV MFMA two
+  // transposing reads (four ahead) and 3 vector ops
   __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
 #pragma unroll
   for (int j = 0; j < 2 * G::NK; ++j) {
     __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
     if (j + 2 < 2 * G::NK) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedVALU, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVector, 5, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
 #pragma unroll
   for (int j = 0; j < 4 * G::ND; ++j) {
     __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
     if (j + 2 < 4 * G::ND) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVector, 3, 0);
   }
 }
 
