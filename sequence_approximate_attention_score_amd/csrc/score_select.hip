@@ -7,8 +7,9 @@
 // query row r % l_q):
 //     s[g, j] = sum_r softmax_{j' in block v}(scale * q_r . k_j')_j
 // Three kernels, all with a fixed reduction order (results are bitwise reproducible):
-//   1. row statistics: per (block, KV head, 128-row group, 2048-key split) the running max
-//      (log2 units) and sum of exp2 of each row; S^T = K . Q^T on MFMA puts one row per lane.
+//   1. row statistics: per (block, KV head, 128-row group, 2048-key split) a running offset
+//      (at most kTau below the row max, log2 units) and the sum of exp2 relative to it;
+//      S^T = K . Q^T on MFMA puts one row per lane.
 //   2. column sums: per (block, KV head, 256-key tile) the split statistics are folded into
 //      each row's log-sum-exp, S = Q . K^T is recomputed on MFMA (one key per lane) and the
 //      probabilities are summed down the rows.
@@ -26,6 +27,7 @@ constexpr int kThreads = 256;
 constexpr int kKeyTile = 64;        // keys per LDS tile in the row-statistics kernel
 constexpr int kColKeys = 256;       // keys per column-sum workgroup (64 per wave)
 constexpr int kQChunk = 128;        // query rows staged in LDS at a time (column sums)
+constexpr float kTau = 8.0f;        // log2 headroom of the lazy row offset (row statistics)
 
 // ------------------------------------------------------------------ 1. row statistics
 template <int D>
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void score_rowstats(const ScoreParams p) 
   };
   fetch(k_begin);
   int buf = 0;
-  float m = -INFINITY, l = 0.f;   // raw-logit max, sum of exp2((s - m) * c) over this lane's keys
+  float m = -INFINITY, l = 0.f;   // raw-logit offset, sum of exp2((s - m) * c) over this lane's keys
   for (int k0 = k_begin; k0 < k_end; k0 += kKeyTile, buf ^= 1) {
     const int valid = min(kKeyTile, k_end - k0);
     uint16_t* sKb = sK + buf * kKeyTile * KSTR;
@@ -98,25 +100,32 @@ __global__ __launch_bounds__(kThreads) void score_rowstats(const ScoreParams p) 
         const bf16x8 a = as_bf16x8(load16(sKb + (n * 32 + l32) * KSTR + ks * 16 + half * 8));
         s[n] = mfma32(a, qf[ks], s[n]);
       }
+    if (valid < kKeyTile) {   // ragged last tile: keys past the split end drop out
+#pragma unroll
+      for (int n = 0; n < kKeyTile / 32; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = n * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+          s[n][r] = kk >= valid ? -INFINITY : s[n][r];
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int n = 0; n < kKeyTile / 32; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = n * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-        if (kk >= valid) s[n][r] = -INFINITY;
-        mx = fmaxf(mx, s[n][r]);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
     mx = fmaxf(mx, swap_half(mx));
-    const float mn = fmaxf(m, mx);
-    float acc = l * fast_exp2((m - mn) * p.scale_log2);
-    if (m == -INFINITY) acc = 0.f;
+    // lazy offset: raised only when the tile maximum exceeds it by more than kTau (log2
+    // units), so every exponential stays <= 2^kTau; the first tile always raises it
+    if ((mx - m) * p.scale_log2 > kTau) {
+      l = m == -INFINITY ? 0.f : l * fast_exp2((m - mx) * p.scale_log2);
+      m = mx;
+    }
+    const float mc = m * p.scale_log2;
 #pragma unroll
     for (int n = 0; n < kKeyTile / 32; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc += fast_exp2((s[n][r] - mn) * p.scale_log2);
-    m = mn;
-    l = acc;
+      for (int r = 0; r < 16; ++r) l += fast_exp2(fmaf(s[n][r], p.scale_log2, -mc));
   }
   l += swap_half(l);
   if (half == 0 && row < p.rows) {
@@ -206,8 +215,9 @@ __global__ __launch_bounds__(kThreads) void score_colsum(const ScoreParams p, in
     }
     __syncthreads();
     if (c0 + kQChunk < p.rows) fetch(c0 + kQChunk);
-    const int nrb = min(kQChunk, p.rows - c0 + 31) / 32;
-    for (int rb = 0; rb < nrb; ++rb) {
+    // one 32-row block: S = Q.K^T for the wave's two 32-key groups, probabilities summed
+    // into the column totals (rows past the end have lse = +inf and add 0)
+    auto row_block = [&](int rb) {
       bf16x8 af[NK];
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks)
@@ -228,6 +238,15 @@ __global__ __launch_bounds__(kThreads) void score_colsum(const ScoreParams p, in
         for (int r = 0; r < 16; ++r) acc += fast_exp2(fmaf(s[r], p.scale_log2, -lse[r]));
         col[kg] += acc;
       }
+    };
+    const int nrb = min(kQChunk, p.rows - c0 + 31) / 32;
+    if (nrb == kQChunk / 32) {
+      // a full chunk as one straight-line block, so the exponentials of one row block
+      // overlap the MFMAs of the next
+#pragma unroll
+      for (int rb = 0; rb < kQChunk / 32; ++rb) row_block(rb);
+    } else {
+      for (int rb = 0; rb < nrb; ++rb) row_block(rb);
     }
   }
 #pragma unroll
