@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "approx-attn prefill tokens/s per layer at 128K ctx; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 ATTN_SOURCES = ["sequence_approximate_attention_score_amd/csrc/attn.hip",
-                "sequence_approximate_attention_score_amd/csrc/attn_core.h",
+                "sequence_approximate_attention_score_amd/csrc/attn_pipe.h",
                 "sequence_approximate_attention_score_amd/csrc/apbv_device.h",
                 "sequence_approximate_attention_score_amd/csrc/apbv_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_c2_traffic.txt")

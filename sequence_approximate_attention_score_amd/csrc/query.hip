@@ -8,37 +8,32 @@
 // Two kernels:
 //  1. query_partial_kernel: one workgroup = 8 waves x 32 rows over one chunk of keys of
 //     one KV head (the chunk length is chosen so that the grid fills whole rounds of the
-//     256 compute units). The rows are the G heads of the KV group times the
-//     l_q query rows, packed into the MFMA row dimension, so each K/V tile staged in LDS
-//     serves the whole group. It writes the chunk's normalised fp32 output and lse.
+//     256 compute units), through the pipelined tile loop of attn_pipe.h. The rows are the
+//     G heads of the KV group times the l_q query rows, packed into the MFMA row
+//     dimension, so each K/V tile staged in LDS serves the whole group. It writes the
+//     chunk's normalised fp32 output and lse.
 //  2. query_merge_kernel: one wave per (head, row) folds the chunks through their lse and
 //     writes the bf16 output and the row's lse.
 #include "apbv_device.h"
 #include "apbv_internal.h"
-#include "attn_core.h"
+#include "attn_pipe.h"
 
 namespace apbv {
 
 namespace {
 
-using tile::attend_tile;
-using tile::KeySrc;
-using tile::load_tile;
-using tile::LoadMap;
-using tile::Shape;
-
-constexpr int kWaves = 8, kKeys = 64;
-constexpr int kRows = kWaves * 32;    // packed rows per workgroup
-constexpr int kNoCausal = 1 << 30;
+using namespace pipe;
 
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void query_partial_kernel(const QueryParams p) {
-  using S = Shape<D, kWaves, 1, kKeys>;
-  constexpr int NK = D / 16, ND = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * S::STAGE];
-  LoadMap<D, kWaves, 1, kKeys> lm;
-  lm.init();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[G::KELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t K1[G::KELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[G::VELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t V1[G::VELEMS];
+  Loader<D> ld;
+  ld.init();
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
 
   // workgroup -> (row tile, KV head, chunk); the row tiles of one chunk and KV head read the
@@ -89,74 +84,63 @@ __global__ __launch_bounds__(kWaves * 64) void query_partial_kernel(const QueryP
   const int pmin = straight ? first : 0;
   const int pmax = straight ? first + 31 : p.l_query - 1;
 
-  bf16x8 qf[1][NK];
+  bf16x8 qf[G::NK];
   {
     const uint16_t* qrow = p.qq + ((int64_t)i * p.hq + h) * D + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) qf[0][ks] = as_bf16x8(load16(qrow + ks * 16));
+    for (int ks = 0; ks < G::NK; ++ks) qf[ks] = as_bf16x8(load16(qrow + ks * 16));
   }
-  f32x16 o[1][ND];
-  float m_run[1] = {-INFINITY}, l_run[1] = {0.f};
+  f32x16 o[G::ND];
 #pragma unroll
-  for (int db = 0; db < ND; ++db)
+  for (int db = 0; db < G::ND; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[0][db][e] = 0.f;
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
-  const int ntiles = (len + kKeys - 1) / kKeys;
+  const int ntiles = (len + kKT - 1) / kKT;
+  // tiles this wave computes: all of them, except that a causal chunk ends for the wave at
+  // its last query position, and a wave past the packed rows computes nothing
+  const int n_live = !wave_live ? 0
+                     : !causal  ? ntiles
+                     : pmax < kpos0 ? 0 : min(ntiles, (pmax - kpos0) / kKT + 1);
   auto source = [&](int t) -> KeySrc {
     KeySrc s;
-    s.k = kb + (int64_t)t * kKeys * stride;
-    s.v = vb + (int64_t)t * kKeys * stride;
+    s.k = kb + (int64_t)t * kKT * stride;
+    s.v = vb + (int64_t)t * kKT * stride;
     s.stride = stride;
-    s.valid = min(kKeys, len - t * kKeys);
+    s.valid = min(kKT, len - t * kKT);
     return s;
   };
-
-  load_tile<D, kWaves, 1, kKeys>(lds, lm, source(0));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile<D, kWaves, 1, kKeys>(lds + (buf ^ 1) * S::STAGE, lm, source(t + 1));
-    const uint16_t* stage = lds + buf * S::STAGE;
-    const int key0 = kpos0 + t * kKeys;
-    const int valid = min(kKeys, len - t * kKeys);
-    const bool skip = !wave_live || (causal && key0 > pmax);
-    if (!skip) {
-      const bool need_mask = valid < kKeys || (causal && key0 + kKeys - 1 > pmin);
-      if (need_mask) {
-        const int pos[1] = {causal ? i : kNoCausal};
-        attend_tile<D, kWaves, 1, kKeys, true>(stage, qf, o, m_run, l_run, p.scale_log2, key0,
-                                               valid, pos);
-      } else {
-        const int pos[1] = {0};
-        attend_tile<D, kWaves, 1, kKeys, false>(stage, qf, o, m_run, l_run, p.scale_log2, key0,
-                                                valid, pos);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  auto mask_of = [&](int t) {
+    TileMask m;
+    m.key0 = kpos0 + t * kKT;
+    m.valid = min(kKT, len - t * kKT);
+    m.mask = m.valid < kKT || (causal && m.key0 + kKT - 1 > pmin);
+    m.pos = causal ? i : kNoCausal;
+    return m;
+  };
+  run_tiles<D>(ntiles, n_live, source, mask_of, qf, o, m_run, l_run, p.scale_log2, K0, K1, V0,
+               V1, ld);
 
   // normalised partial output (fp32) and natural-log lse; a row that saw no key of this
   // chunk (causal chunk past the row) gets output 0 and lse -inf
-  const float lt = l_run[0] + swap_half(l_run[0]);
+  const float lt = l_run + swap_half(l_run);
   if (r < n_rows) {
     const int64_t prow = ((int64_t)c * p.hq + h) * p.l_query + i;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     float* orow = p.part_o + prow * D;
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+    for (int db = 0; db < G::ND; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = db * 32 + 8 * q4 + 4 * half;
-        const f32x16& ov = o[0][db];
+        const f32x16& ov = o[db];
         float4 w = {ov[4 * q4 + 0] * inv, ov[4 * q4 + 1] * inv, ov[4 * q4 + 2] * inv,
                     ov[4 * q4 + 3] * inv};
         *reinterpret_cast<float4*>(orow + d0) = w;
       }
     if (half == 0)
-      p.part_lse[prow] = lt > 0.f ? (m_run[0] + fast_log2(lt)) * 0.69314718055994531f : -INFINITY;
+      p.part_lse[prow] = lt > 0.f ? (m_run + fast_log2(lt)) * 0.69314718055994531f : -INFINITY;
   }
 }
 
