@@ -1,0 +1,86 @@
+"""Host-side arithmetic and contract of bench.py (CPU only, no kernel is launched)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from synthetic import workload  # noqa: E402
+
+
+def visible_pairs_brute(block_starts, l_anchor, l_pass):
+    """(row, key) pairs one query head attends to, counted from an explicit mask over
+    [anchor | passing of every block | context]: row i of block v sees the anchor, the
+    passing rows of blocks < v and its own block's keys up to i."""
+    bs = list(block_starts)
+    n = len(bs) - 1
+    n_keys = l_anchor + n * l_pass + bs[-1]
+    total = 0
+    for v in range(n):
+        for i in range(bs[v], bs[v + 1]):
+            mask = np.zeros(n_keys, bool)
+            mask[:l_anchor] = True
+            mask[l_anchor:l_anchor + v * l_pass] = True
+            ctx0 = l_anchor + n * l_pass
+            mask[ctx0 + bs[v]:ctx0 + i + 1] = True
+            total += int(mask.sum())
+    return total
+
+
+def test_attention_flops_match_a_brute_force_mask_count():
+    bs, la, lp, hq, d = [0, 7, 20, 26, 40], 5, 3, 6, 64
+    pairs = visible_pairs_brute(bs, la, lp)
+    assert bench.attention_flops(bs, la, lp, hq, d) == pairs * hq * 4 * d
+
+
+def test_attention_flops_at_128k_match_the_config_arithmetic():
+    # 16 blocks of 8192, anchor 2048, l_p 1024, 28 query heads, d = 128: 1.812e9 visible
+    # pairs per head (anchor 0.27e9, passing 1.01e9, local 0.54e9) -> 25.98 TFLOP
+    w = workload("c2")
+    bs = np.arange(0, 16 * 8192 + 1, 8192)
+    anchor = 16 * 8192 * 2048
+    passing = sum(8192 * v * 1024 for v in range(16))
+    local = 16 * (8192 * 8193 // 2)
+    assert (anchor, passing, local) == (268435456, 1006632960, 536936448)
+    flops = bench.attention_flops(bs, w.l_anchor, w.l_pass, w.hq, w.head_dim)
+    assert flops == (anchor + passing + local) * 28 * 4 * 128
+    assert abs(flops - 2.598e13) / 2.598e13 < 1e-3
+
+
+def test_gather_bytes_at_128k_are_72_mib():
+    class Lay:
+        hkv, pre_rows = 4, 2048 + 16 * 1024
+    assert bench.gather_bytes(Lay, 128) == 72 * 2**20
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_is_reported_only_for_the_profiled_kernel_source(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.txt"
+    f.write_text("# header\nkernel_source_sha256: %s\ntraffic_bytes_per_launch: 1.5e10\n"
+                 % bench.attn_source_sha())
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.read_traffic() == pytest.approx(1.5e10)
+    f.write_text("kernel_source_sha256: %s\ntraffic_bytes_per_launch: 1.5e10\n" % ("0" * 64))
+    assert bench.read_traffic() is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
+    assert bench.read_traffic() is None
+
+
+def test_committed_traffic_summary_matches_the_current_attention_source():
+    """The committed counter summary must describe the kernel as it is now (a change to the
+    attention sources needs new FETCH_SIZE / WRITE_SIZE passes)."""
+    t = bench.read_traffic()
+    assert t is not None and 1e9 < t < 1e11
