@@ -14,10 +14,10 @@
 //    O += V_i^T P_i^T runs beside the row sums of tile i and the row maxima of tile i + 1.
 //    The instruction order is fixed with scheduling groups so that every MFMA has vector
 //    work issued behind it. K tiles therefore run one tile ahead of V tiles: two K buffers
-//    and two V buffers (separate LDS arrays, padded rows: K +16 B, V +32 B), filled by
-//    buffer loads straight into LDS; the loads of K_{i+2} and V_{i+1} are in flight during
-//    iteration i, one barrier per iteration. The loop is unrolled by two so that every LDS
-//    access names its array statically.
+//    and two V buffers (separate LDS arrays, padded rows: K +16 B, V +64 B, so that neither
+//    operand read has bank conflicts), filled by buffer loads straight into LDS; the loads
+//    of K_{i+2} and V_{i+1} are in flight during iteration i, one barrier per iteration.
+//    The loop is unrolled by two so that every LDS access names its array statically.
 //  * Online softmax in log2 units with a lazy rescale: the running offset is only raised
 //    when a tile's maximum exceeds it by more than 8 (probabilities stay <= 256), which is
 //    exact up to rounding and skips almost every O rescale. Mask code runs only on tiles
@@ -77,7 +77,11 @@ constexpr int kSchedVector = kSchedVALU | kSchedTrans;
 template <int D>
 struct Geo {
   static constexpr int KSTR = D + 8;               // K row stride in LDS (elements)
-  static constexpr int VSTR = D + 16;              // V row stride in LDS (elements)
+  // V row stride in LDS (elements): a transposing read serves 32 lanes per pass, four
+  // rows x two 32-byte column groups; a row stride of 16 or 48 mod 64 banks (dwords; d =
+  // 128 gives 80, d = 64 gives 48) spreads the four rows 16 banks apart, so the eight
+  // 8-bank pieces cover the 64 banks once
+  static constexpr int VSTR = D + 32;
   static constexpr int KSLOT = KSTR / 8;           // 16-byte slots per padded row
   static constexpr int VSLOT = VSTR / 8;
   static constexpr int SEGK = kKT * KSLOT / 64;    // 1 KB load segments per K tile
