@@ -15,7 +15,7 @@
 //      probabilities are summed down the rows.
 //   3. selection: per (block, KV head) an exact radix select of the l_p-th largest score on
 //      order-preserving 32-bit keys, then a stable compaction (ties to the lower row) that
-//      writes the chosen rows in ascending order.
+//      writes the chosen rows in ascending order, placed by block-wide prefix sums.
 #include "apbv_device.h"
 #include "apbv_internal.h"
 
@@ -262,10 +262,42 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over the workgroup's threads in thread order (wsum: 4 words of LDS).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(x);
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  __syncthreads();   // wsum is reused by the next scan
+  return before + inc - x;
+}
+
+// One workgroup per (block, KV head).
+//  * Radix select on order-preserving 32-bit keys, 8 bits per pass from the top, finds the
+//    exact l_pass-th largest key T and how many keys equal to T are still needed. Each wave
+//    counts into its own histogram (less atomic contention); wave 0 sums them and finds the
+//    digit with one suffix scan over its lanes (lane l holds digits 4l .. 4l+3).
+//  * Stable compaction in row order: thread t owns a contiguous run of rows. It counts its
+//    keys above T and equal to T; an exclusive scan of the equal counts gives how many tied
+//    rows come before its run (ties go to the lower rows), a second scan of the rows it
+//    keeps gives its output position.
 __global__ __launch_bounds__(kThreads) void select_topk(const ScoreParams p) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kThreads / 64][256];
   __shared__ uint32_t sh_prefix, sh_need;
-  __shared__ uint32_t wave_cnt[2][kThreads / 64];
+  __shared__ uint32_t wsum[kThreads / 64];
 
   const int v = blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
   const int lo = p.bs[v], hi = p.bs[v + 1];
@@ -274,63 +306,68 @@ __global__ __launch_bounds__(kThreads) void select_topk(const ScoreParams p) {
   if (p.l_pass == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // radix select, most significant byte first: find the exact l_pass-th largest key
   uint32_t prefix = 0, need = (uint32_t)p.l_pass;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-    hist[tid] = 0;
+    for (int i = tid; i < (kThreads / 64) * 256; i += kThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
     for (int j = lo + tid; j < hi; j += kThreads) {
       const uint32_t k = order_key(sc[j]);
-      if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[wave][(k >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t acc = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (acc + hist[d] >= need) break;
-        acc += hist[d];
+    if (wave == 0) {
+      uint32_t b[4], s = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        b[e] = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) b[e] += hist[w][4 * lane + e];
+        s += b[e];
       }
-      sh_prefix = prefix | ((uint32_t)d << shift);
-      sh_need = need - acc;
+      const uint32_t incl = wave_incl_scan(s);
+      const uint32_t above = __shfl(incl, 63) - incl;   // keys with a digit of a higher lane
+      // exactly one lane holds the digit d with count(digit > d) < need <= count(digit >= d)
+      if (above < need && need <= above + s) {
+        uint32_t acc = above;
+        int d = 4 * lane;
+        for (int e = 3; e >= 0; --e) {
+          d = 4 * lane + e;
+          if (acc + b[e] >= need) break;
+          acc += b[e];
+        }
+        sh_prefix = prefix | ((uint32_t)d << shift);
+        sh_need = need - acc;
+      }
     }
     __syncthreads();
     prefix = sh_prefix;
     need = sh_need;
-    __syncthreads();
   }
-  // prefix = threshold key T; take every key > T and the first `need` keys == T (by row)
+
   const uint32_t T = prefix;
-  uint32_t base_sel = 0, base_eq = 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int j0 = lo; j0 < hi; j0 += kThreads) {
-    const int j = j0 + tid;
-    const uint32_t k = j < hi ? order_key(sc[j]) : 0u;
-    const bool eq = j < hi && k == T;
-    const uint64_t eq_b = __ballot(eq);
-    __syncthreads();
-    if (lane == 0) wave_cnt[0][wave] = __popcll(eq_b);
-    __syncthreads();
-    uint32_t eq_before = base_eq;
-    for (int w = 0; w < wave; ++w) eq_before += wave_cnt[0][w];
-    eq_before += __popcll(eq_b & lt_mask);
-    const bool take = j < hi && (k > T || (eq && eq_before < need));
-    const uint64_t tk_b = __ballot(take);
-    if (lane == 0) wave_cnt[1][wave] = __popcll(tk_b);
-    __syncthreads();
-    uint32_t pos = base_sel;
-    for (int w = 0; w < wave; ++w) pos += wave_cnt[1][w];
-    pos += __popcll(tk_b & lt_mask);
-    if (take) out[pos] = j;
-    uint32_t tot_eq = 0, tot_sel = 0;
-    for (int w = 0; w < kThreads / 64; ++w) {
-      tot_eq += wave_cnt[0][w];
-      tot_sel += wave_cnt[1][w];
+  const int L = hi - lo;
+  const int run = (L + kThreads - 1) / kThreads;
+  const int r0 = lo + min(tid * run, L), r1 = lo + min((tid + 1) * run, L);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int j = r0; j < r1; ++j) {
+    const uint32_t k = order_key(sc[j]);
+    n_gt += k > T;
+    n_eq += k == T;
+  }
+  const uint32_t eq_before = block_excl_scan(n_eq, wsum);
+  const uint32_t eq_take = eq_before >= need ? 0u : min(n_eq, need - eq_before);
+  uint32_t pos = block_excl_scan(n_gt + eq_take, wsum);
+  uint32_t eq_seen = 0;
+  for (int j = r0; j < r1; ++j) {
+    const uint32_t k = order_key(sc[j]);
+    if (k > T) {
+      out[pos++] = j;
+    } else if (k == T) {
+      if (eq_seen < eq_take) out[pos++] = j;
+      ++eq_seen;
     }
-    base_eq += tot_eq;
-    base_sel += tot_sel;
   }
 }
 

@@ -84,6 +84,14 @@ def full_check(x, lay, *, rows=None, heads=None, blocks=None):
         n_band = sum(_sel_one(s32, g["sel"], bs, lay.l_pass, v) for v in blocks)
         say(f"  selection: equal outside the tie band ({n_band} band positions)")
     attempt("selection", sel_check)
+
+    def sel_rule_check():
+        # the selection rule itself, bit-exact whatever the score rounding: the oracle's
+        # top-l_p (ties to the lower row) of the GPU's own fp32 scores gives the GPU's rows
+        own = orc.select_passing(g["scores"], bs, lay.l_pass)
+        for v in blocks:
+            assert np.array_equal(own[v], g["sel"][v]), (v, "selection of the GPU's scores")
+    attempt("selection rule", sel_rule_check)
     # gather: bitwise against the oracle's gather of the GPU's own selection
     kp, vp = orc.gather_prefix(ka, va, kc, vc, g["sel"])
 
@@ -113,6 +121,37 @@ def _sel_one(s32, sel, bs, l_pass, v):
 
 def small(name="c0", **kw):
     return generate(workload(name, **kw))
+
+
+def test_selection_ties_go_to_the_lower_row():
+    """Exact ties at the selection threshold: every block's keys repeat a 7-row pattern, so
+    bitwise-equal keys give bitwise-equal scores, and the l_p-th largest score is shared by
+    rows on both sides of the cut. The GPU must keep the lowest rows of the tied group,
+    as the oracle's stable ranking of the same scores does."""
+    x = small("c0", hq=4, hkv=2, l_query=16, l_pass=24)
+    bs = np.asarray(x.block_starts)
+    kb = x.bits["k_ctx"].copy()
+    for v in range(len(bs) - 1):
+        lo, hi = int(bs[v]), int(bs[v + 1])
+        kb[lo:hi] = kb[lo + (np.arange(hi - lo) % 7)]
+    x.bits["k_ctx"] = kb
+    lay = layout_of(x)
+    g = run_gpu(x, lay, upload(x))
+    own = orc.select_passing(g["scores"], bs, lay.l_pass)
+    assert np.array_equal(own, g["sel"])
+    n_split = 0
+    for v in range(len(bs) - 1):
+        lo, hi = int(bs[v]), int(bs[v + 1])
+        for kv in range(lay.hkv):
+            blk = g["scores"][kv, lo:hi]
+            t = np.sort(blk)[::-1][lay.l_pass - 1]
+            tied = np.flatnonzero(blk == t) + lo
+            chosen = np.isin(tied, g["sel"][v, kv])
+            if chosen.any() and not chosen.all():
+                n_split += 1
+                # the chosen members of the tied group are its lowest rows
+                assert np.all(tied[chosen] < tied[~chosen].min()), (v, kv)
+    assert n_split > 0, "no tie straddles the threshold"
 
 
 # ------------------------------------------------------------------------- small, exhaustive
