@@ -5,8 +5,10 @@ One step = one layer of the hot path on the 128K-token Qwen2.5-VL-7B-shaped work
 anchor 2048, query block 128, l_p 1024): score_select -> gather_passing ->
 approx_attn_prefill, with every input already resident in HBM. Prints one JSON line.
 Beside the timed steps it also times the query block's rows (query_forward), each ZigZag
-bucket's attention alone, the attention with the last-level cache flushed, and one layer
-for each layout of the bucket sweep (2, 4, 6, 8 buckets) and of the anchor-only baseline.
+bucket's attention alone, the attention with the last-level cache flushed, the one-call
+layer (prefill_layer) on one stream and with the selection of later blocks on a second
+stream beside the attention, and one layer for each layout of the bucket sweep (2, 4, 6, 8
+buckets) and of the anchor-only baseline.
 
     python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
                     [--profile] [--calib-copy]
@@ -235,6 +237,23 @@ def main():
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         cold_ms = median_ms(attention, 5, before=lambda: flush.fill_(1))
         del flush
+    # the one-call layer (apbv_prefill_layer): the three steps in order on one stream, and
+    # with the selection and gather of later blocks on a second stream beside the attention
+    layer_one_ms = layer_two_ms = None
+    if not args.profile:
+        aux = torch.cuda.Stream()
+
+        def one_call(aux_s=None):
+            apbv.prefill_layer(lay, d["q_query"], d["q_ctx"], d["k_ctx"], d["v_ctx"],
+                               d["k_anchor"], d["v_anchor"], aux_stream=aux_s, sel=sel,
+                               k_pre=kp, v_pre=vp, out=out, workspace=ws)
+        one_call()
+        one_call(aux)
+        torch.cuda.synchronize()
+        layer_one_ms = median_ms(one_call, 9)
+        layer_two_ms = median_ms(lambda: one_call(aux), 9)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        plan = apbv.prefill_layer_plan(lay, cus)
     # the bucket-count sweep (2, 4, 6, 8 buckets) and the anchor-only baseline (l_p = 0) on
     # the same context, each as one layer: score_select -> gather_passing -> attention
     sweep = []
@@ -314,6 +333,11 @@ def main():
                                  if bucket_ms else None),
         "query_forward_ms": q_ms,
         "layer_with_query_rows_tokens_per_s": (x.N + w.l_query) / ((ms_step + q_ms) * 1e-3),
+        "layer_one_call_ms": layer_one_ms,
+        "layer_two_stream_ms": layer_two_ms,
+        "layer_two_stream_tokens_per_s": x.N / (layer_two_ms * 1e-3) if layer_two_ms else None,
+        "layer_two_stream_plan": ({"late_bucket_begin": plan[0], "early_blocks": plan[1]}
+                                  if layer_two_ms else None),
         "gather_GBps": gather_bytes(lay, w.head_dim) / (float(per[:, 1].mean()) * 1e-3) / 1e9,
         "sweep": sweep or None,
         "cpu_baseline": None,

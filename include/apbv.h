@@ -140,6 +140,47 @@ apbv_status apbv_approx_attn_prefill(const apbv_layout* layout, const apbv_bf16*
                                      apbv_bf16* out, float* lse, int32_t range_begin,
                                      int32_t range_end, void* stream);
 
+/*
+ * One layer of steps 1-3 with the selection and gather of later blocks overlapped with
+ * attention (same page, Metodologia, "Comunicazione Sovrapposta": moving the passing blocks
+ * runs beside the attention computation; on one GPU the producer of the passing blocks is
+ * the scoring, selection and gather of the later blocks). Results are bit-identical to
+ * apbv_score_select + apbv_gather_passing + apbv_approx_attn_prefill over the same buffers.
+ *
+ *   q_query, k_ctx, scores, sel, workspace, workspace_bytes: as apbv_score_select
+ *   k_anchor, v_anchor, v_ctx, k_pre, v_pre:                 as apbv_gather_passing
+ *   q_ctx, out, lse:                                         as apbv_approx_attn_prefill
+ *   stream      hipStream_t all work is ordered on: on return the whole layer is enqueued
+ *               there (work on the aux stream is joined back into it)
+ *   aux_stream  a second hipStream_t of the same device, or NULL (then the three steps run
+ *               in order on stream)
+ *   ready_event, done_event  two hipEvent_t of the device, owned by the caller, recorded by
+ *               this call (needed with aux_stream; calls that overlap in time must not share
+ *               them)
+ * With aux_stream, stream runs: selection and gather of blocks [0, early), attention of
+ * buckets [late, n_buckets), then (after the aux stream) attention of buckets [0, late);
+ * aux_stream runs the selection and gather of blocks [early, n) beside the first attention
+ * launch. (late, early) come from apbv_prefill_layer_plan with the device's compute units.
+ */
+apbv_status apbv_prefill_layer(const apbv_layout* layout, const apbv_bf16* q_query,
+                               const apbv_bf16* q_ctx, const apbv_bf16* k_ctx,
+                               const apbv_bf16* v_ctx, const apbv_bf16* k_anchor,
+                               const apbv_bf16* v_anchor, float* scores, int32_t* sel,
+                               apbv_bf16* k_pre, apbv_bf16* v_pre, apbv_bf16* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               void* aux_stream, void* ready_event, void* done_event);
+
+/*
+ * Host only: the split apbv_prefill_layer uses on a device with compute_units CUs.
+ * Attention of ZigZag buckets [late, n_buckets) needs the selections of blocks [0, early)
+ * only (bucket b holds blocks b and n-1-b, so early = n-1-late); late is the largest bucket
+ * index whose late set of workgroups fills whole rounds of the compute units (one attention
+ * workgroup per CU at a time), else 0 with early = n-1. With l_pass = 0, or zigzag = 0 (a
+ * late block set always contains the last block), late = 0; early = 0 when l_pass = 0.
+ */
+apbv_status apbv_prefill_layer_plan(const apbv_layout* layout, int32_t compute_units,
+                                    int32_t* late_bucket_begin, int32_t* early_blocks);
+
 /* Workspace bytes needed by apbv_query_forward for this layout (written to *bytes; 0 when
  * l_query is 0). */
 apbv_status apbv_query_forward_workspace(const apbv_layout* layout, size_t* bytes);

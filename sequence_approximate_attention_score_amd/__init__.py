@@ -4,17 +4,20 @@ The hot path is three C-ABI calls backed by hand-written HIP kernels (``libapbv.
 ``score_select`` (query-to-context scores + per-KV-head top-l_p passing selection),
 ``gather_passing`` (anchor + passing blocks into one prefix per KV head) and
 ``approx_attn_prefill`` (bf16 MFMA attention over [anchor | passing | causal local] with a
-ZigZag work schedule), plus ``query_forward`` for the rows of the query block (exact
-attention over the whole sequence, partial results merged through their lse). This package
-is the thin Python binding over that library.
+ZigZag work schedule), ``prefill_layer`` (the three in one call, optionally with the
+selection of later blocks on a second stream beside the attention), plus ``query_forward``
+for the rows of the query block (exact attention over the whole sequence, partial results
+merged through their lse). This package is the thin Python binding over that library.
 """
 from ._lib import (ApbvError, Layout, approx_attn_prefill, attn_tile_rows, gather_passing,
-                   lib, num_buckets, query_forward, query_forward_workspace, schedule,
-                   score_select, score_select_workspace, version)
+                   lib, num_buckets, prefill_layer, prefill_layer_plan, query_forward,
+                   query_forward_workspace, schedule, score_select, score_select_workspace,
+                   version)
 
 __all__ = ["ApbvError", "Layout", "approx_attn_prefill", "attn_tile_rows", "gather_passing",
-           "lib", "num_buckets", "query_forward", "query_forward_workspace", "schedule",
-           "score_select", "score_select_workspace", "version", "run_layer"]
+           "lib", "num_buckets", "prefill_layer", "prefill_layer_plan", "query_forward",
+           "query_forward_workspace", "schedule", "score_select", "score_select_workspace",
+           "version", "run_layer"]
 
 
 def run_layer(layout: Layout, q_query, q_ctx, k_ctx, v_ctx, k_anchor, v_anchor, *, workspace=None,

@@ -21,7 +21,7 @@ MAX_BLOCKS = 64
 EXPORTED = ["apbv_score_select_workspace", "apbv_score_select", "apbv_gather_passing",
             "apbv_approx_attn_prefill", "apbv_query_forward_workspace", "apbv_query_forward",
             "apbv_num_buckets", "apbv_schedule", "apbv_attn_tile_rows", "apbv_status_str",
-            "apbv_last_error", "apbv_version"]
+            "apbv_last_error", "apbv_version", "apbv_prefill_layer", "apbv_prefill_layer_plan"]
 
 
 class ApbvError(RuntimeError):
@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
             "apbv_query_forward_workspace": (_I32, [_LP, ctypes.POINTER(_SZ)]),
             "apbv_query_forward": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           _SZ, _VP]),
+            "apbv_prefill_layer": (_I32, [_LP] + [_VP] * 13 + [_SZ] + [_VP] * 4),
+            "apbv_prefill_layer_plan": (_I32, [_LP, _I32, ctypes.POINTER(_I32),
+                                               ctypes.POINTER(_I32)]),
             "apbv_num_buckets": (_I32, [_LP]),
             "apbv_schedule": (_I32, [_LP, _I32, _I32, _VP, _I32, ctypes.POINTER(_I32)]),
             "apbv_attn_tile_rows": (_I32, [_I32]),
@@ -297,6 +300,82 @@ def query_forward(layout: Layout, q_query, k_query, v_query, k_anchor, v_anchor,
     _check(lib().apbv_query_forward(L.ref(), *args, workspace.numel(), _stream(dev)),
            "apbv_query_forward")
     return out, lse
+
+
+def prefill_layer_plan(layout: Layout, compute_units: int) -> tuple[int, int]:
+    """(late, early) of the two-stream layer: attention of buckets [late, n_buckets) runs
+    after the selections of blocks [0, early) only (host only)."""
+    late, early = _I32(0), _I32(0)
+    _check(lib().apbv_prefill_layer_plan(layout.ref(), compute_units, ctypes.byref(late),
+                                         ctypes.byref(early)), "apbv_prefill_layer_plan")
+    return late.value, early.value
+
+
+_layer_events: dict = {}
+
+
+def _events(dev):
+    """Two events of the device for apbv_prefill_layer (created once per device and kept
+    alive; layer calls on one device from several threads at once must not share them)."""
+    import torch
+    key = torch.device(dev).index or 0
+    if key not in _layer_events:
+        evs = (torch.cuda.Event(), torch.cuda.Event())
+        for e in evs:
+            e.record(torch.cuda.current_stream(dev))   # creates the underlying event
+        _layer_events[key] = evs
+    return _layer_events[key]
+
+
+def prefill_layer(layout: Layout, q_query, q_ctx, k_ctx, v_ctx, k_anchor, v_anchor, *,
+                  aux_stream=None, scores=None, sel=None, k_pre=None, v_pre=None, out=None,
+                  lse=None, want_scores: bool = False, want_lse: bool = False, workspace=None):
+    """Steps 1-3 of one layer in one call; with ``aux_stream`` (a torch.cuda.Stream of the
+    same device) the selection and gather of later blocks overlap attention. Returns
+    (out, lse or None, sel, scores or None)."""
+    import torch
+    dev = k_ctx.device
+    L, d, bf = layout, layout.head_dim, torch.bfloat16
+    if want_scores and scores is None:
+        scores = torch.empty((L.hkv, L.n_tokens), dtype=torch.float32, device=dev)
+    if sel is None:
+        sel = torch.empty((L.n_blocks, L.hkv, L.l_pass), dtype=torch.int32, device=dev)
+    shape = (L.hkv, L.pre_rows, d)
+    if k_pre is None:
+        k_pre = torch.empty(shape, dtype=bf, device=dev)
+    if v_pre is None:
+        v_pre = torch.empty(shape, dtype=bf, device=dev)
+    if out is None:
+        out = torch.empty((L.n_tokens, L.hq, d), dtype=bf, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((L.hq, L.n_tokens), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(score_select_workspace(layout), 256), dtype=torch.uint8,
+                                device=dev)
+    has_anchor, has_pre = L.l_anchor > 0, L.pre_rows > 0
+    args = _pointers(
+        _arg(q_query, "q_query", bf, L.l_query, L.hq * d, required=L.l_query > 0),
+        _arg(q_ctx, "q_ctx", bf, L.n_tokens, L.hq * d, L.q_stride),
+        _arg(k_ctx, "k_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(v_ctx, "v_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(k_anchor, "k_anchor", bf, L.l_anchor, L.hkv * d, required=has_anchor),
+        _arg(v_anchor, "v_anchor", bf, L.l_anchor, L.hkv * d, required=has_anchor),
+        _arg(scores, "scores", torch.float32, L.hkv, L.n_tokens, required=False),
+        _arg(sel, "sel", torch.int32, L.n_blocks, L.hkv * L.l_pass),
+        _arg(k_pre, "k_pre", bf, L.hkv, L.pre_rows * d, required=has_pre),
+        _arg(v_pre, "v_pre", bf, L.hkv, L.pre_rows * d, required=has_pre),
+        _arg(out, "out", bf, L.n_tokens, L.hq * d),
+        _arg(lse, "lse", torch.float32, L.hq, L.n_tokens, required=False),
+        _arg(workspace, "workspace", torch.uint8, workspace.numel(), 1))
+    aux = ready = done = None
+    if aux_stream is not None:
+        if aux_stream.device != dev:
+            raise ValueError("aux_stream must be a stream of the tensors' device")
+        aux = aux_stream.cuda_stream
+        ready, done = (e.cuda_event for e in _events(dev))
+    _check(lib().apbv_prefill_layer(L.ref(), *args[:12], args[12], workspace.numel(),
+                                    _stream(dev), aux, ready, done), "apbv_prefill_layer")
+    return out, lse, sel, scores
 
 
 def version() -> str:

@@ -121,6 +121,7 @@ struct ScoreParams {
   int64_t kv_stride;
   int32_t hq, hkv, group, l_query, rows;   // rows = group * l_query
   int32_t n_tokens, n_blocks, n_split, l_pass;
+  int32_t v_begin, v_count;   // blocks scored and selected by one launch
   float scale_log2;
   int32_t bs[APBV_MAX_BLOCKS + 1];
 };
@@ -146,6 +147,7 @@ struct GatherParams {
   uint16_t* vpre;
   int64_t kv_stride;
   int32_t hkv, l_anchor, l_pass, n_blocks, pre_rows, n_tokens;
+  int32_t row_begin, row_count;   // prefix rows written by one launch
 };
 
 hipError_t launch_gather(const GatherParams& p, int head_dim, hipStream_t stream);

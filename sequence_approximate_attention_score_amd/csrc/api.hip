@@ -118,11 +118,160 @@ void build_schedule(Schedule& s, int32_t n_blocks, const int32_t* bs, int32_t zi
   }
 }
 
+namespace {
+
+// Checks of the scoring call and its parameters for blocks [v_begin, v_begin + v_count).
+apbv_status score_params(const apbv_layout* layout, const Checked& c, const apbv_bf16* q_query,
+                         const apbv_bf16* k_ctx, float* scores, int32_t* sel, void* workspace,
+                         size_t workspace_bytes, ScoreParams& p) {
+  APBV_TRY(check_ptr(q_query, "q_query", c.l_q > 0));
+  APBV_TRY(check_ptr(k_ctx, "k_ctx", true));
+  APBV_TRY(check_ptr(sel, "sel", c.l_p > 0));
+  if (scores != nullptr && ((uintptr_t)scores & 3u) != 0)
+    return fail(APBV_EINVAL, "scores is not 4-byte aligned");
+  const int rows = c.G * c.l_q;
+  if (score_colsum_lds_bytes(rows, c.d) > kMaxLdsBytes)
+    return fail(APBV_EUNSUPPORTED, "G * l_query = %d score rows exceed the column-sum LDS", rows);
+  const int n_split = n_split_of(c);
+  const size_t need = score_workspace_bytes(c.n, c.hkv, rows, n_split, c.N, scores == nullptr);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(APBV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (workspace != nullptr && ((uintptr_t)workspace & 255u) != 0)
+    return fail(APBV_EINVAL, "workspace is not 256-byte aligned");
+
+  memset(&p, 0, sizeof(p));
+  p.qq = q_query;
+  p.kc = k_ctx;
+  p.stats = reinterpret_cast<float2*>(workspace);
+  const size_t stats_bytes = (((size_t)c.n * c.hkv * n_split * rows * sizeof(float2)) + 255) & ~(size_t)255;
+  p.scores = scores != nullptr ? scores
+                               : reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes);
+  p.sel = sel;
+  p.kv_stride = c.kv_stride;
+  p.hq = c.hq;
+  p.hkv = c.hkv;
+  p.group = c.G;
+  p.l_query = c.l_q;
+  p.rows = rows;
+  p.n_tokens = c.N;
+  p.n_blocks = c.n;
+  p.n_split = n_split;
+  p.l_pass = c.l_p;
+  p.v_begin = 0;
+  p.v_count = c.n;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+  for (int v = 0; v <= c.n; ++v) p.bs[v] = layout->block_starts[v];
+  return APBV_OK;
+}
+
+// Checks of the gather call and its parameters for prefix rows [row_begin, row_begin + count).
+apbv_status gather_params(const Checked& c, const apbv_bf16* k_anchor, const apbv_bf16* v_anchor,
+                          const apbv_bf16* k_ctx, const apbv_bf16* v_ctx, const int32_t* sel,
+                          apbv_bf16* k_pre, apbv_bf16* v_pre, GatherParams& p) {
+  APBV_TRY(check_ptr(k_anchor, "k_anchor", c.l_a > 0));
+  APBV_TRY(check_ptr(v_anchor, "v_anchor", c.l_a > 0));
+  APBV_TRY(check_ptr(k_ctx, "k_ctx", c.l_p > 0));
+  APBV_TRY(check_ptr(v_ctx, "v_ctx", c.l_p > 0));
+  APBV_TRY(check_ptr(sel, "sel", c.l_p > 0));
+  APBV_TRY(check_ptr(k_pre, "k_pre", c.pre_rows > 0));
+  APBV_TRY(check_ptr(v_pre, "v_pre", c.pre_rows > 0));
+  memset(&p, 0, sizeof(p));
+  p.ka = k_anchor;
+  p.va = v_anchor;
+  p.kc = k_ctx;
+  p.vc = v_ctx;
+  p.sel = sel;
+  p.kpre = k_pre;
+  p.vpre = v_pre;
+  p.kv_stride = c.kv_stride;
+  p.hkv = c.hkv;
+  p.l_anchor = c.l_a;
+  p.l_pass = c.l_p;
+  p.n_blocks = c.n;
+  p.pre_rows = c.pre_rows;
+  p.n_tokens = c.N;
+  p.row_begin = 0;
+  p.row_count = c.pre_rows;
+  return APBV_OK;
+}
+
+// Checks of the attention call and its parameters for the whole schedule (the caller picks
+// the unit range).
+apbv_status attn_params(const apbv_layout* layout, const Checked& c, const apbv_bf16* q_ctx,
+                        const apbv_bf16* k_pre, const apbv_bf16* v_pre, const apbv_bf16* k_ctx,
+                        const apbv_bf16* v_ctx, apbv_bf16* out, float* lse, AttnParams& p) {
+  APBV_TRY(check_ptr(q_ctx, "q_ctx", true));
+  APBV_TRY(check_ptr(k_ctx, "k_ctx", true));
+  APBV_TRY(check_ptr(v_ctx, "v_ctx", true));
+  APBV_TRY(check_ptr(k_pre, "k_pre", c.pre_rows > 0));
+  APBV_TRY(check_ptr(v_pre, "v_pre", c.pre_rows > 0));
+  APBV_TRY(check_ptr(out, "out", true));
+  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return fail(APBV_EINVAL, "lse is not 4-byte aligned");
+  if ((int64_t)c.hq * c.N > 0x7fffffffLL * 8) return fail(APBV_EUNSUPPORTED, "problem too large");
+  memset(&p, 0, sizeof(p));
+  build_schedule(p.sched, c.n, layout->block_starts, layout->zigzag, attn_tile_rows(c.d));
+  p.q = q_ctx;
+  p.kpre = k_pre;
+  p.vpre = v_pre;
+  p.kc = k_ctx;
+  p.vc = v_ctx;
+  p.out = out;
+  p.lse = lse;
+  p.q_stride = c.q_stride;
+  p.kv_stride = c.kv_stride;
+  p.hq = c.hq;
+  p.hkv = c.hkv;
+  p.group = c.G;
+  p.l_anchor = c.l_a;
+  p.l_pass = c.l_p;
+  p.pre_rows = c.pre_rows;
+  p.n_tokens = c.N;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+  return APBV_OK;
+}
+
+// Launch of the attention over buckets (zigzag) or blocks [range_begin, range_end).
+apbv_status launch_attn_range(AttnParams& p, const Checked& c, int range_begin, int range_end,
+                              hipStream_t stream) {
+  p.unit_begin = p.sched.units_before(range_begin);
+  p.n_units = p.sched.units_before(range_end) - p.unit_begin;
+  if ((uint64_t)p.n_units * (uint64_t)p.hq >= (1ull << 32))
+    return fail(APBV_EUNSUPPORTED, "grid too large");
+  const hipError_t e = launch_attention(p, c.d, stream);
+  if (e != hipSuccess) return fail(APBV_EHIP, "attention launch: %s", hipGetErrorString(e));
+  return APBV_OK;
+}
+
+// Split of one layer for the two-stream overlap. Attention of the buckets [late, n_buckets)
+// needs the selections of blocks [0, early) only: with ZigZag, bucket b holds blocks b and
+// n-1-b, so the late set's highest block is n-1-late and early = n-1-late. The late set is
+// the smallest one whose workgroups (one per CU at a time) fill whole rounds of the compute
+// units, so that splitting the attention into two launches adds no partial round; late = 0
+// (one attention launch, only the last block scored beside it) when none does. Without
+// passing blocks nothing is selected before attention: late = 0, early = 0.
+void plan_layer(const Checked& c, const Schedule& s, int compute_units, int& late, int& early) {
+  const int nb = s.n_buckets();
+  late = 0;
+  early = c.l_p == 0 ? 0 : c.n - 1;
+  if (c.l_p == 0 || !s.zigzag || compute_units <= 0) return;
+  for (int b = nb - 1; b >= 1; --b) {
+    const int64_t wgs = (int64_t)(s.units_before(nb) - s.units_before(b)) * c.hq;
+    if (wgs % compute_units == 0) {
+      late = b;
+      early = c.n - 1 - b;
+      return;
+    }
+  }
+}
+
+}  // namespace
 }  // namespace apbv
 
 using namespace apbv;
 
 extern "C" {
+
 
 const char* apbv_version(void) { return "apbv-gfx950 0.1.0"; }
 
@@ -161,43 +310,8 @@ apbv_status apbv_score_select(const apbv_layout* layout, const apbv_bf16* q_quer
                               void* workspace, size_t workspace_bytes, void* stream) {
   Checked c;
   APBV_TRY(check_layout(layout, c));
-  APBV_TRY(check_ptr(q_query, "q_query", c.l_q > 0));
-  APBV_TRY(check_ptr(k_ctx, "k_ctx", true));
-  APBV_TRY(check_ptr(sel, "sel", c.l_p > 0));
-  if (scores != nullptr && ((uintptr_t)scores & 3u) != 0)
-    return fail(APBV_EINVAL, "scores is not 4-byte aligned");
-  const int rows = c.G * c.l_q;
-  if (score_colsum_lds_bytes(rows, c.d) > kMaxLdsBytes)
-    return fail(APBV_EUNSUPPORTED, "G * l_query = %d score rows exceed the column-sum LDS", rows);
-  const int n_split = n_split_of(c);
-  const size_t need = score_workspace_bytes(c.n, c.hkv, rows, n_split, c.N, scores == nullptr);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(APBV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  if (workspace != nullptr && ((uintptr_t)workspace & 255u) != 0)
-    return fail(APBV_EINVAL, "workspace is not 256-byte aligned");
-
   ScoreParams p;
-  memset(&p, 0, sizeof(p));
-  p.qq = q_query;
-  p.kc = k_ctx;
-  p.stats = reinterpret_cast<float2*>(workspace);
-  const size_t stats_bytes = (((size_t)c.n * c.hkv * n_split * rows * sizeof(float2)) + 255) & ~(size_t)255;
-  p.scores = scores != nullptr ? scores
-                               : reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes);
-  p.sel = sel;
-  p.kv_stride = c.kv_stride;
-  p.hq = c.hq;
-  p.hkv = c.hkv;
-  p.group = c.G;
-  p.l_query = c.l_q;
-  p.rows = rows;
-  p.n_tokens = c.N;
-  p.n_blocks = c.n;
-  p.n_split = n_split;
-  p.l_pass = c.l_p;
-  p.scale_log2 = c.scale * 1.4426950408889634f;
-  for (int v = 0; v <= c.n; ++v) p.bs[v] = layout->block_starts[v];
+  APBV_TRY(score_params(layout, c, q_query, k_ctx, scores, sel, workspace, workspace_bytes, p));
   const hipError_t e = launch_score_select(p, c.d, c.max_block, (hipStream_t)stream);
   if (e != hipSuccess) return fail(APBV_EHIP, "score/select launch: %s", hipGetErrorString(e));
   g_err[0] = 0;
@@ -210,29 +324,8 @@ apbv_status apbv_gather_passing(const apbv_layout* layout, const apbv_bf16* k_an
                                 apbv_bf16* v_pre, void* stream) {
   Checked c;
   APBV_TRY(check_layout(layout, c));
-  APBV_TRY(check_ptr(k_anchor, "k_anchor", c.l_a > 0));
-  APBV_TRY(check_ptr(v_anchor, "v_anchor", c.l_a > 0));
-  APBV_TRY(check_ptr(k_ctx, "k_ctx", c.l_p > 0));
-  APBV_TRY(check_ptr(v_ctx, "v_ctx", c.l_p > 0));
-  APBV_TRY(check_ptr(sel, "sel", c.l_p > 0));
-  APBV_TRY(check_ptr(k_pre, "k_pre", c.pre_rows > 0));
-  APBV_TRY(check_ptr(v_pre, "v_pre", c.pre_rows > 0));
   GatherParams p;
-  memset(&p, 0, sizeof(p));
-  p.ka = k_anchor;
-  p.va = v_anchor;
-  p.kc = k_ctx;
-  p.vc = v_ctx;
-  p.sel = sel;
-  p.kpre = k_pre;
-  p.vpre = v_pre;
-  p.kv_stride = c.kv_stride;
-  p.hkv = c.hkv;
-  p.l_anchor = c.l_a;
-  p.l_pass = c.l_p;
-  p.n_blocks = c.n;
-  p.pre_rows = c.pre_rows;
-  p.n_tokens = c.N;
+  APBV_TRY(gather_params(c, k_anchor, v_anchor, k_ctx, v_ctx, sel, k_pre, v_pre, p));
   const hipError_t e = launch_gather(p, c.d, (hipStream_t)stream);
   if (e != hipSuccess) return fail(APBV_EHIP, "gather launch: %s", hipGetErrorString(e));
   g_err[0] = 0;
@@ -272,45 +365,94 @@ apbv_status apbv_approx_attn_prefill(const apbv_layout* layout, const apbv_bf16*
                                      int32_t range_end, void* stream) {
   Checked c;
   APBV_TRY(check_layout(layout, c));
-  APBV_TRY(check_ptr(q_ctx, "q_ctx", true));
-  APBV_TRY(check_ptr(k_ctx, "k_ctx", true));
-  APBV_TRY(check_ptr(v_ctx, "v_ctx", true));
-  APBV_TRY(check_ptr(k_pre, "k_pre", c.pre_rows > 0));
-  APBV_TRY(check_ptr(v_pre, "v_pre", c.pre_rows > 0));
-  APBV_TRY(check_ptr(out, "out", true));
-  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return fail(APBV_EINVAL, "lse is not 4-byte aligned");
-  if ((int64_t)c.hq * c.N > 0x7fffffffLL * 8) return fail(APBV_EUNSUPPORTED, "problem too large");
-
   AttnParams p;
-  memset(&p, 0, sizeof(p));
-  build_schedule(p.sched, c.n, layout->block_starts, layout->zigzag, attn_tile_rows(c.d));
+  APBV_TRY(attn_params(layout, c, q_ctx, k_pre, v_pre, k_ctx, v_ctx, out, lse, p));
   const int nb = p.sched.n_buckets();
   if (range_begin == 0 && range_end == 0) range_end = nb;
   if (range_begin < 0 || range_end > nb || range_begin > range_end)
     return fail(APBV_EINVAL, "range [%d, %d) outside [0, %d]", range_begin, range_end, nb);
-  p.q = q_ctx;
-  p.kpre = k_pre;
-  p.vpre = v_pre;
-  p.kc = k_ctx;
-  p.vc = v_ctx;
-  p.out = out;
-  p.lse = lse;
-  p.q_stride = c.q_stride;
-  p.kv_stride = c.kv_stride;
-  p.hq = c.hq;
-  p.hkv = c.hkv;
-  p.group = c.G;
-  p.l_anchor = c.l_a;
-  p.l_pass = c.l_p;
-  p.pre_rows = c.pre_rows;
-  p.n_tokens = c.N;
-  p.scale_log2 = c.scale * 1.4426950408889634f;
-  p.unit_begin = p.sched.units_before(range_begin);
-  p.n_units = p.sched.units_before(range_end) - p.unit_begin;
-  if ((uint64_t)p.n_units * (uint64_t)p.hq >= (1ull << 32))
-    return fail(APBV_EUNSUPPORTED, "grid too large");
-  const hipError_t e = launch_attention(p, c.d, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(APBV_EHIP, "attention launch: %s", hipGetErrorString(e));
+  APBV_TRY(launch_attn_range(p, c, range_begin, range_end, (hipStream_t)stream));
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_prefill_layer_plan(const apbv_layout* layout, int32_t compute_units,
+                                    int32_t* late_bucket_begin, int32_t* early_blocks) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  if (late_bucket_begin == nullptr || early_blocks == nullptr)
+    return fail(APBV_EINVAL, "late_bucket_begin / early_blocks is NULL");
+  Schedule s;
+  build_schedule(s, c.n, layout->block_starts, layout->zigzag, attn_tile_rows(c.d));
+  int late, early;
+  plan_layer(c, s, compute_units, late, early);
+  *late_bucket_begin = late;
+  *early_blocks = early;
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_prefill_layer(const apbv_layout* layout, const apbv_bf16* q_query,
+                               const apbv_bf16* q_ctx, const apbv_bf16* k_ctx,
+                               const apbv_bf16* v_ctx, const apbv_bf16* k_anchor,
+                               const apbv_bf16* v_anchor, float* scores, int32_t* sel,
+                               apbv_bf16* k_pre, apbv_bf16* v_pre, apbv_bf16* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               void* aux_stream, void* ready_event, void* done_event) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  ScoreParams sp;
+  APBV_TRY(score_params(layout, c, q_query, k_ctx, scores, sel, workspace, workspace_bytes, sp));
+  GatherParams gp;
+  APBV_TRY(gather_params(c, k_anchor, v_anchor, k_ctx, v_ctx, sel, k_pre, v_pre, gp));
+  AttnParams ap;
+  APBV_TRY(attn_params(layout, c, q_ctx, k_pre, v_pre, k_ctx, v_ctx, out, lse, ap));
+  const int nb = ap.sched.n_buckets();
+  hipStream_t s0 = (hipStream_t)stream;
+  hipError_t e;
+  if (aux_stream == nullptr) {   // the three steps in order on one stream
+    if ((e = launch_score_select(sp, c.d, c.max_block, s0)) != hipSuccess ||
+        (e = launch_gather(gp, c.d, s0)) != hipSuccess)
+      return fail(APBV_EHIP, "layer launch: %s", hipGetErrorString(e));
+    APBV_TRY(launch_attn_range(ap, c, 0, nb, s0));
+    g_err[0] = 0;
+    return APBV_OK;
+  }
+  if (ready_event == nullptr || done_event == nullptr)
+    return fail(APBV_EINVAL, "an aux stream needs ready_event and done_event");
+  if (aux_stream == stream) return fail(APBV_EINVAL, "aux_stream is the main stream");
+  int dev = 0, cus = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess ||
+      (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return fail(APBV_EHIP, "device query: %s", hipGetErrorString(e));
+  int late, early;
+  plan_layer(c, ap.sched, cus, late, early);
+  hipStream_t s1 = (hipStream_t)aux_stream;
+  hipEvent_t ready = (hipEvent_t)ready_event, done = (hipEvent_t)done_event;
+  const int split_row = c.l_a + early * c.l_p;
+  // main stream: the early blocks' selections and prefix rows, then the late buckets
+  sp.v_begin = 0;
+  sp.v_count = early;
+  gp.row_begin = 0;
+  gp.row_count = split_row;
+  if ((e = launch_score_select(sp, c.d, c.max_block, s0)) != hipSuccess ||
+      (e = launch_gather(gp, c.d, s0)) != hipSuccess ||
+      (e = hipEventRecord(ready, s0)) != hipSuccess)
+    return fail(APBV_EHIP, "layer launch: %s", hipGetErrorString(e));
+  APBV_TRY(launch_attn_range(ap, c, late, nb, s0));
+  // aux stream, once the main stream has reached the attention: the remaining blocks
+  sp.v_begin = early;
+  sp.v_count = c.n - early;
+  gp.row_begin = split_row;
+  gp.row_count = c.pre_rows - split_row;
+  if ((e = hipStreamWaitEvent(s1, ready, 0)) != hipSuccess ||
+      (e = launch_score_select(sp, c.d, c.max_block, s1)) != hipSuccess ||
+      (e = launch_gather(gp, c.d, s1)) != hipSuccess ||
+      (e = hipEventRecord(done, s1)) != hipSuccess ||
+      (e = hipStreamWaitEvent(s0, done, 0)) != hipSuccess)
+    return fail(APBV_EHIP, "layer launch: %s", hipGetErrorString(e));
+  // main stream: the early buckets, after the aux stream's selections and prefix rows
+  APBV_TRY(launch_attn_range(ap, c, 0, late, s0));
   g_err[0] = 0;
   return APBV_OK;
 }

@@ -17,15 +17,15 @@ constexpr int kThreads = 256;
 template <int D>
 __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherParams p) {
   constexpr int CH = D / 8;   // 16-byte chunks per row
-  const int64_t per_tensor = (int64_t)p.hkv * p.pre_rows * CH;
+  const int64_t per_tensor = (int64_t)p.hkv * p.row_count * CH;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= 2 * per_tensor) return;
   const int tensor = (int)(idx / per_tensor);
   int64_t rem = idx - tensor * per_tensor;
   const int ch = (int)(rem % CH);
   rem /= CH;
-  const int row = (int)(rem % p.pre_rows);
-  const int g = (int)(rem / p.pre_rows);
+  const int row = p.row_begin + (int)(rem % p.row_count);
+  const int g = (int)(rem / p.row_count);
 
   const uint16_t* src;
   if (row < p.l_anchor) {
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherParams p) 
 }  // namespace
 
 hipError_t launch_gather(const GatherParams& p, int head_dim, hipStream_t stream) {
-  const int64_t total = 2 * (int64_t)p.hkv * p.pre_rows * (head_dim / 8);
+  const int64_t total = 2 * (int64_t)p.hkv * p.row_count * (head_dim / 8);
   if (total == 0) return hipSuccess;
   dim3 grid((uint32_t)((total + kThreads - 1) / kThreads));
   if (head_dim == 128)

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void score_rowstats(const ScoreParams p) 
   const int split = b % p.n_split; b /= p.n_split;
   const int rg = b % n_rg; b /= n_rg;
   const int g = b % p.hkv;
-  const int v = b / p.hkv;
+  const int v = p.v_begin + b / p.hkv;
   const int lo = p.bs[v], hi = p.bs[v + 1];
   const int k_begin = lo + split * kScoreSplit;
   if (k_begin >= hi) return;   // the combiner reads only splits that hold keys
@@ -143,11 +143,11 @@ __global__ __launch_bounds__(kThreads) void score_colsum(const ScoreParams p, in
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem);                   // [2][kQChunk][QSTR]
   float* sL = reinterpret_cast<float*>(smem + 2 * kQChunk * QSTR * 2); // [rows_pad] lse2
 
-  const int n_kt = (gridDim.x / (p.n_blocks * p.hkv));
+  const int n_kt = (gridDim.x / (p.v_count * p.hkv));
   int b = blockIdx.x;
   const int kt = b % n_kt; b /= n_kt;
   const int g = b % p.hkv;
-  const int v = b / p.hkv;
+  const int v = p.v_begin + b / p.hkv;
   const int lo = p.bs[v], hi = p.bs[v + 1];
   const int kbase = lo + kt * kColKeys;
   if (kbase >= hi) return;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void select_topk(const ScoreParams p) {
   __shared__ uint32_t sh_prefix, sh_need;
   __shared__ uint32_t wsum[kThreads / 64];
 
-  const int v = blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
+  const int v = p.v_begin + blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
   const int lo = p.bs[v], hi = p.bs[v + 1];
   const float* sc = p.scores + (int64_t)g * p.n_tokens;
   int32_t* out = p.sel + ((int64_t)v * p.hkv + g) * p.l_pass;
@@ -388,9 +388,10 @@ size_t score_colsum_lds_bytes(int rows, int head_dim) {
 
 hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block,
                                hipStream_t stream) {
+  if (p.v_count <= 0) return hipSuccess;
   const int n_rg = (p.rows + 127) / 128;
   if (p.rows > 0) {
-    dim3 grid(p.n_blocks * p.hkv * n_rg * p.n_split);
+    dim3 grid(p.v_count * p.hkv * n_rg * p.n_split);
     if (head_dim == 128)
       hipLaunchKernelGGL(score_rowstats<128>, grid, dim3(kThreads), 0, stream, p);
     else
@@ -402,7 +403,7 @@ hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block
     const int n_kt = (max_block + kColKeys - 1) / kColKeys;
     const int rows_pad = ((p.rows + kQChunk - 1) / kQChunk) * kQChunk;
     const size_t shm = score_colsum_lds_bytes(p.rows, head_dim);
-    dim3 grid(p.n_blocks * p.hkv * n_kt);
+    dim3 grid(p.v_count * p.hkv * n_kt);
     if (head_dim == 128)
       hipLaunchKernelGGL(score_colsum<128>, grid, dim3(kThreads), shm, stream, p, rows_pad);
     else
@@ -411,7 +412,7 @@ hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block
     if (e != hipSuccess) return e;
   }
   if (p.l_pass > 0) {
-    hipLaunchKernelGGL(select_topk, dim3(p.n_blocks * p.hkv), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(select_topk, dim3(p.v_count * p.hkv), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -290,3 +290,63 @@ def test_binding_accepts_row_strided_views_of_a_fused_projection():
     packed = cpu_inputs(small_layout())                          # packed k_ctx, strided layout
     with pytest.raises(ValueError, match="apart"):
         apbv.score_select(lay, t["q_query"], packed["k_ctx"])
+
+
+def layer_plan_reference(lay, cus):
+    """Plan of the two-stream layer from the schedule itself: the largest bucket b whose
+    buckets [b, n_buckets) hold a multiple of `cus` workgroups (units x hq), else 0."""
+    nb = apbv.num_buckets(lay)
+    if lay.l_pass == 0:
+        return 0, 0
+    if not lay.c.zigzag:
+        return 0, lay.n_blocks - 1
+    for b in range(nb - 1, 0, -1):
+        if apbv.schedule(lay, b, nb).shape[0] * lay.hq % cus == 0:
+            return b, lay.n_blocks - 1 - b
+    return 0, lay.n_blocks - 1
+
+
+@pytest.mark.parametrize("case", [
+    dict(bs=list(range(0, 16 * 8192 + 1, 8192)), la=2048, lp=1024, hq=28, hkv=4, cus=256),
+    dict(bs=list(range(0, 16 * 8192 + 1, 8192)), la=2048, lp=1024, hq=28, hkv=4, cus=304),
+    dict(bs=list(range(0, 32 * 8192 + 1, 8192)), la=2048, lp=1024, hq=28, hkv=4, cus=256),
+    dict(bs=[0, 300, 700, 1000, 1500, 1900], la=64, lp=40, hq=8, hkv=2, cus=8),
+    dict(bs=list(range(0, 16 * 8192 + 1, 8192)), la=2048, lp=0, hq=28, hkv=4, cus=256),
+    dict(bs=list(range(0, 16 * 8192 + 1, 8192)), la=2048, lp=1024, hq=28, hkv=4, cus=256,
+         zigzag=False),
+])
+def test_layer_plan(case):
+    lay = apbv.Layout(case["bs"], l_anchor=case["la"], l_query=16, l_pass=case["lp"],
+                      hq=case["hq"], hkv=case["hkv"], head_dim=128,
+                      zigzag=case.get("zigzag", True))
+    late, early = _lib.prefill_layer_plan(lay, case["cus"])
+    assert (late, early) == layer_plan_reference(lay, case["cus"])
+    # every block a late bucket holds needs only selections of blocks below `early`
+    nb = apbv.num_buckets(lay)
+    if lay.l_pass > 0:
+        for u in apbv.schedule(lay, late, nb):
+            for blk in (u[0], u[2]):
+                assert blk < 0 or blk <= early
+    if case["cus"] == 256 and case["lp"] and case.get("zigzag", True) and len(case["bs"]) == 17:
+        assert (late, early) == (6, 9)   # 128K: buckets 6 and 7 are 1792 workgroups, 7 rounds
+
+
+def test_layer_call_rejects_bad_stream_arguments_before_launch():
+    lay = small_layout()
+    L = apbv.lib()
+    ws = ctypes.c_size_t(0)
+    assert L.apbv_score_select_workspace(lay.ref(), ctypes.byref(ws)) == 0
+    ptrs = [0x1000 * (i + 1) for i in range(13)]
+    base = dict(zip(["qq", "qc", "kc", "vc", "ka", "va", "sc", "sel", "kp", "vp", "out", "lse",
+                     "ws"], ptrs))
+
+    def call(aux, ready, done, stream=0x9000, **over):
+        p = dict(base, **over)
+        return L.apbv_prefill_layer(lay.ref(), p["qq"], p["qc"], p["kc"], p["vc"], p["ka"],
+                                    p["va"], p["sc"], p["sel"], p["kp"], p["vp"], p["out"],
+                                    p["lse"], p["ws"], ws.value, stream, aux, ready, done)
+    assert call(0xA000, None, 0xC000) == _lib.APBV_EINVAL      # aux stream without events
+    assert call(0xA000, 0xB000, None) == _lib.APBV_EINVAL
+    assert call(0x9000, 0xB000, 0xC000) == _lib.APBV_EINVAL    # aux stream == main stream
+    assert call(0xA000, 0xB000, 0xC000, out=0x6008) == _lib.APBV_EINVAL   # misaligned out
+    assert call(0xA000, 0xB000, 0xC000, ws=None) == _lib.APBV_EWORKSPACE
