@@ -11,8 +11,9 @@
  *      (apbv_gather_passing),
  *   3. runs attention of the block's rows over [anchor | passing blocks of the preceding
  *      blocks | the block's own keys, causal]                        (apbv_approx_attn_prefill).
- * The rows of the query block itself, which see the whole sequence, come from
- * apbv_query_forward.
+ * apbv_prefill_layer runs the three steps in one call, optionally with the selection of later
+ * blocks on a second stream beside the attention. The rows of the query block itself, which
+ * see the whole sequence, come from apbv_query_forward.
  * All virtual blocks of the method's sequence-parallel layout live on one GPU; ZigZag
  * pairing of block p with block n-1-p (same page, "Suddivisione del Contesto e
  * Disposizione ZigZag" and "Bilanciamento del Carico dell'Attenzione Approssimata") is the
@@ -32,7 +33,8 @@
  *    = 0, block_starts[n_blocks] = N (context tokens; anchor and query block excluded).
  *  - Every argument is validated before anything is enqueued; on error nothing is launched
  *    and the call returns a non-zero apbv_status (apbv_last_error() gives details for the
- *    calling thread). A failed launch returns APBV_EHIP.
+ *    calling thread). A failed launch returns APBV_EHIP (apbv_prefill_layer may have
+ *    enqueued its earlier launches by then).
  *  - Calls on one stream may be issued from several threads; the library keeps no mutable
  *    global state apart from the per-thread error message.
  */
