@@ -372,3 +372,33 @@ def test_outputs_stay_in_bounds():
         assert torch.all(buf[:4096] == fill) and torch.all(buf[-4096:] == fill), name
         assert torch.isfinite(view.float()).all() or name == "sel", name
     say("  guards intact around every output")
+
+
+def test_layer_call_stays_in_bounds():
+    """The one-call layer with a second stream (block and row ranges of the scoring and the
+    gather on both streams) writes only its own outputs and matches the three calls."""
+    x = generate(dataclasses.replace(workload("c0"), name="guard", keys="iid", hq=14, hkv=2,
+                                     head_dim=128, total_tokens=1000, n_blocks=5, block_len=0,
+                                     l_anchor=37, l_query=19, l_pass=21),
+                 block_starts=[0, 129, 300, 555, 700, 1000])
+    lay = layout_of(x)
+    d = upload(x)
+    w = x.w
+    bufs = {"scores": _guarded((w.hkv, x.N), torch.float32, 7.0),
+            "sel": _guarded((lay.n_blocks, w.hkv, lay.l_pass), torch.int32, -7),
+            "k_pre": _guarded((w.hkv, lay.pre_rows, w.head_dim), torch.bfloat16, 7.0),
+            "v_pre": _guarded((w.hkv, lay.pre_rows, w.head_dim), torch.bfloat16, 7.0),
+            "out": _guarded((x.N, w.hq, w.head_dim), torch.bfloat16, 7.0),
+            "lse": _guarded((w.hq, x.N), torch.float32, 7.0)}
+    v = {k: b[1] for k, b in bufs.items()}
+    apbv.prefill_layer(lay, d["q_query"], d["q_ctx"], d["k_ctx"], d["v_ctx"], d["k_anchor"],
+                       d["v_anchor"], aux_stream=torch.cuda.Stream(), **v)
+    torch.cuda.synchronize()
+    for name, (buf, view) in bufs.items():
+        fill = buf[0].item()
+        assert torch.all(buf[:4096] == fill) and torch.all(buf[-4096:] == fill), name
+    g = run_gpu(x, lay, d)
+    assert np.array_equal(v["sel"].cpu().numpy(), g["sel"])
+    assert np.array_equal(v["scores"].cpu().numpy(), g["scores"])
+    assert np.array_equal(host_f64(v["out"]), g["out"])
+    say("  guards intact around every output of the one-call layer")
