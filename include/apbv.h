@@ -159,10 +159,12 @@ apbv_status apbv_approx_attn_prefill(const apbv_layout* layout, const apbv_bf16*
  *   ready_event, done_event  two hipEvent_t of the device, owned by the caller, recorded by
  *               this call (needed with aux_stream; calls that overlap in time must not share
  *               them)
+ *   compute_units  CUs the split is planned for; 0 = the current device's count (other
+ *               values only move the split, never the results)
  * With aux_stream, stream runs: selection and gather of blocks [0, early), attention of
  * buckets [late, n_buckets), then (after the aux stream) attention of buckets [0, late);
  * aux_stream runs the selection and gather of blocks [early, n) beside the first attention
- * launch. (late, early) come from apbv_prefill_layer_plan with the device's compute units.
+ * launch. (late, early) come from apbv_prefill_layer_plan with compute_units.
  */
 apbv_status apbv_prefill_layer(const apbv_layout* layout, const apbv_bf16* q_query,
                                const apbv_bf16* q_ctx, const apbv_bf16* k_ctx,
@@ -170,7 +172,8 @@ apbv_status apbv_prefill_layer(const apbv_layout* layout, const apbv_bf16* q_que
                                const apbv_bf16* v_anchor, float* scores, int32_t* sel,
                                apbv_bf16* k_pre, apbv_bf16* v_pre, apbv_bf16* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               void* aux_stream, void* ready_event, void* done_event);
+                               void* aux_stream, void* ready_event, void* done_event,
+                               int32_t compute_units);
 
 /*
  * Host only: the split apbv_prefill_layer uses on a device with compute_units CUs.

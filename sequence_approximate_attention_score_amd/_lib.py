@@ -58,7 +58,7 @@ def lib() -> ctypes.CDLL:
             "apbv_query_forward_workspace": (_I32, [_LP, ctypes.POINTER(_SZ)]),
             "apbv_query_forward": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           _SZ, _VP]),
-            "apbv_prefill_layer": (_I32, [_LP] + [_VP] * 13 + [_SZ] + [_VP] * 4),
+            "apbv_prefill_layer": (_I32, [_LP] + [_VP] * 13 + [_SZ] + [_VP] * 4 + [_I32]),
             "apbv_prefill_layer_plan": (_I32, [_LP, _I32, ctypes.POINTER(_I32),
                                                ctypes.POINTER(_I32)]),
             "apbv_num_buckets": (_I32, [_LP]),
@@ -329,10 +329,11 @@ def _events(dev):
 
 def prefill_layer(layout: Layout, q_query, q_ctx, k_ctx, v_ctx, k_anchor, v_anchor, *,
                   aux_stream=None, scores=None, sel=None, k_pre=None, v_pre=None, out=None,
-                  lse=None, want_scores: bool = False, want_lse: bool = False, workspace=None):
+                  lse=None, want_scores: bool = False, want_lse: bool = False, workspace=None,
+                  compute_units: int = 0):
     """Steps 1-3 of one layer in one call; with ``aux_stream`` (a torch.cuda.Stream of the
-    same device) the selection and gather of later blocks overlap attention. Returns
-    (out, lse or None, sel, scores or None)."""
+    same device) the selection and gather of later blocks overlap attention, split for
+    ``compute_units`` CUs (0: the device's). Returns (out, lse or None, sel, scores or None)."""
     import torch
     dev = k_ctx.device
     L, d, bf = layout, layout.head_dim, torch.bfloat16
@@ -374,7 +375,8 @@ def prefill_layer(layout: Layout, q_query, q_ctx, k_ctx, v_ctx, k_anchor, v_anch
         aux = aux_stream.cuda_stream
         ready, done = (e.cuda_event for e in _events(dev))
     _check(lib().apbv_prefill_layer(L.ref(), *args[:12], args[12], workspace.numel(),
-                                    _stream(dev), aux, ready, done), "apbv_prefill_layer")
+                                    _stream(dev), aux, ready, done, int(compute_units)),
+           "apbv_prefill_layer")
     return out, lse, sel, scores
 
 

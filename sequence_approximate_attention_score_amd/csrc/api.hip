@@ -398,7 +398,8 @@ apbv_status apbv_prefill_layer(const apbv_layout* layout, const apbv_bf16* q_que
                                const apbv_bf16* v_anchor, float* scores, int32_t* sel,
                                apbv_bf16* k_pre, apbv_bf16* v_pre, apbv_bf16* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               void* aux_stream, void* ready_event, void* done_event) {
+                               void* aux_stream, void* ready_event, void* done_event,
+                               int32_t compute_units) {
   Checked c;
   APBV_TRY(check_layout(layout, c));
   ScoreParams sp;
@@ -421,10 +422,14 @@ apbv_status apbv_prefill_layer(const apbv_layout* layout, const apbv_bf16* q_que
   if (ready_event == nullptr || done_event == nullptr)
     return fail(APBV_EINVAL, "an aux stream needs ready_event and done_event");
   if (aux_stream == stream) return fail(APBV_EINVAL, "aux_stream is the main stream");
-  int dev = 0, cus = 0;
-  if ((e = hipGetDevice(&dev)) != hipSuccess ||
-      (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-    return fail(APBV_EHIP, "device query: %s", hipGetErrorString(e));
+  if (compute_units < 0) return fail(APBV_EINVAL, "compute_units = %d", compute_units);
+  int cus = compute_units;
+  if (cus == 0) {
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess ||
+        (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return fail(APBV_EHIP, "device query: %s", hipGetErrorString(e));
+  }
   int late, early;
   plan_layer(c, ap.sched, cus, late, early);
   hipStream_t s1 = (hipStream_t)aux_stream;

@@ -341,12 +341,14 @@ def test_layer_call_rejects_bad_stream_arguments_before_launch():
                      "ws"], ptrs))
 
     def call(aux, ready, done, stream=0x9000, **over):
-        p = dict(base, **over)
+        p = dict(base, **{k: v for k, v in over.items() if k != "cus"})
         return L.apbv_prefill_layer(lay.ref(), p["qq"], p["qc"], p["kc"], p["vc"], p["ka"],
                                     p["va"], p["sc"], p["sel"], p["kp"], p["vp"], p["out"],
-                                    p["lse"], p["ws"], ws.value, stream, aux, ready, done)
+                                    p["lse"], p["ws"], ws.value, stream, aux, ready, done,
+                                    over.get("cus", 0))
     assert call(0xA000, None, 0xC000) == _lib.APBV_EINVAL      # aux stream without events
     assert call(0xA000, 0xB000, None) == _lib.APBV_EINVAL
     assert call(0x9000, 0xB000, 0xC000) == _lib.APBV_EINVAL    # aux stream == main stream
     assert call(0xA000, 0xB000, 0xC000, out=0x6008) == _lib.APBV_EINVAL   # misaligned out
     assert call(0xA000, 0xB000, 0xC000, ws=None) == _lib.APBV_EWORKSPACE
+    assert call(0xA000, 0xB000, 0xC000, cus=-1) == _lib.APBV_EINVAL

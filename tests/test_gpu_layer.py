@@ -88,3 +88,52 @@ def test_128k_plan_splits_on_this_device():
     if cus == 256:
         assert (late, early) == (6, 9)
     assert 0 <= late < apbv.num_buckets(lay) and early == lay.n_blocks - 1 - late
+
+
+def _random_case(seed):
+    import dataclasses
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(2, 9))
+    lens = rng.integers(40, 700, size=n)
+    bs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 3, 7]))
+    w = dataclasses.replace(workload("c0"), name=f"random{seed}", keys="iid", hq=hq, hkv=hkv,
+                            head_dim=int(rng.choice([64, 128])), total_tokens=int(bs[-1]),
+                            n_blocks=n, block_len=0, l_anchor=int(rng.choice([0, 33, 64])),
+                            l_query=int(rng.integers(1, 24)),
+                            l_pass=int(rng.integers(0, lens.min() + 1)))
+    return generate(w, block_starts=bs.tolist()), rng
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_layer_split_on_random_layouts(seed):
+    """Random ragged layouts with a CU count chosen so that the plan really splits the
+    attention (late > 0): the two-stream layer is bit-identical to the three calls."""
+    x, rng = _random_case(seed)
+    lay = layout_of(x)
+    nb = apbv.num_buckets(lay)
+    cus = 0
+    if nb > 1 and lay.l_pass > 0:
+        b = int(rng.integers(1, nb))
+        cus = apbv.schedule(lay, b, nb).shape[0] * lay.hq
+    late, early = _lib.prefill_layer_plan(lay, cus)
+    say(f"seed {seed}: n={lay.n_blocks} N={lay.n_tokens} hq={lay.hq} hkv={lay.hkv} "
+        f"d={lay.head_dim} l_a={lay.l_anchor} l_p={lay.l_pass} buckets={nb} cus={cus} "
+        f"-> late {late}, early {early}")
+    if cus:
+        assert late >= 1 and early == lay.n_blocks - 1 - late
+    d = upload(x)
+    ref = three_calls(lay, d)
+    shape = (lay.hkv, lay.pre_rows, lay.head_dim)
+    k_pre = torch.full(shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    v_pre = torch.full(shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    out, lse, sel, scores = apbv.prefill_layer(lay, d["q_query"], d["q_ctx"], d["k_ctx"],
+                                               d["v_ctx"], d["k_anchor"], d["v_anchor"],
+                                               aux_stream=torch.cuda.Stream(), k_pre=k_pre,
+                                               v_pre=v_pre, want_scores=True, want_lse=True,
+                                               compute_units=cus)
+    torch.cuda.synchronize()
+    got = dict(out=out, lse=lse, sel=sel, scores=scores, k_pre=k_pre, v_pre=v_pre)
+    for k in ("scores", "sel", "k_pre", "v_pre", "out", "lse"):
+        assert torch.equal(ref[k], got[k]), (seed, k)
