@@ -98,56 +98,148 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(x, budget_s: float = 15.0):
-    """The float64 oracle, as it is, on a bounded sample of the same workload: scores and
-    selection of the middle block for every KV head, and the attention of that block for as
-    many query heads as fit in about ``budget_s`` seconds (one per KV group first);
-    extrapolated to the whole layer by algorithmic work."""
+MAX_POOL_WORKERS = 16   # host cores one GPU's share of the box provides
+
+
+def visible_pairs(block_starts, l_anchor, l_pass, v, row_begin, row_end) -> int:
+    """(row, key) pairs one query head attends to for rows [row_begin, row_end) of block v
+    (offsets inside the block): the whole prefix plus the causal local keys."""
+    P = l_anchor + v * l_pass
+    a, b = int(row_begin), int(row_end)
+    return (b - a) * P + (b * (b + 1) - a * (a + 1)) // 2
+
+
+def _pool_init():
+    """Each pool worker runs the oracle on one core (BLAS pinned to one thread)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # noqa: BLE001
+        pass
+
+
+def _warm(_):
+    """Imports the oracle in a worker (outside the timed parts)."""
+    from oracle import apbv_oracle  # noqa: F401
+    import synthetic  # noqa: F401
+    return os.getpid()
+
+
+def _oracle_score_task(t):
+    """Scores of block v for the G query heads of KV head g (one unit of the oracle's step 1),
+    timed inside the worker."""
+    from oracle import apbv_oracle as orc
+    from synthetic.gen import bits_to_f32
+    q, k = bits_to_f32(t["q_query"]), bits_to_f32(t["k_block"])
+    t0 = time.perf_counter()
+    s = orc.passing_scores(q, k, [0, k.shape[0]], q.shape[1], 1, t["scale"])
+    return t["v"], t["g"], s[0], time.perf_counter() - t0
+
+
+def _oracle_attn_task(t):
+    """Attention of rows [a, b) of block v for the G query heads of KV head g over the block's
+    prefix (anchor + passing of earlier blocks) and its causal local keys, timed inside the
+    worker."""
+    from oracle import apbv_oracle as orc
+    from synthetic.gen import bits_to_f32
+    q = bits_to_f32(t["q_rows"])                   # [b, G, d]: rows 0..b-1 of the block
+    kp, vp = bits_to_f32(t["k_pre"]), bits_to_f32(t["v_pre"])   # [1, P, d]
+    kc, vc = bits_to_f32(t["k_loc"]), bits_to_f32(t["v_loc"])   # [b, 1, d]
+    a, b = t["rows"]
+    t0 = time.perf_counter()
+    orc.attend(q, kp, vp, kc, vc, [0, b], kp.shape[1], 0, q.shape[1], 1, t["scale"],
+               rows=np.arange(a, b))
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(x, tiles_per_unit: int | None = 2, workers: int | None = None, seed: int = 5):
+    """The float64 oracle, as it is, on the host's cores, over a bounded sample of one layer.
+
+    Work is split into (block, KV head) units run by a process pool (spawned workers, BLAS
+    at one thread each): step 1 (scores) for every unit, steps 2-3 (selection, gather) in
+    this process, and step 4 (attention) for ``tiles_per_unit`` seeded 256-row tiles of every
+    unit (``None``: every row). The layer time is the measured selection and gather plus the
+    summed worker time of scores and sampled attention, the latter scaled by all visible
+    (row, key) pairs of all query heads over the sampled ones, divided by the workers.
+    Returns the record and the raw figures it came from."""
+    import concurrent.futures
+    import multiprocessing
     from oracle import apbv_oracle as orc
     w = x.w
-    bs = np.asarray(x.block_starts)
-    n = len(bs) - 1
-    v = n // 2
-    scale = 1.0 / math.sqrt(w.head_dim)
-    qq, kc, vc = x.f32("q_query"), x.f32("k_ctx"), x.f32("v_ctx")
-    t0 = time.perf_counter()
-    s = orc.passing_scores(qq, kc, bs, w.hq, w.hkv, scale, blocks=[v])
-    t_score = time.perf_counter() - t0
-    # selection of every block is needed for the prefix; blocks other than v keep the top rows
-    # of their (unscored) keys by position so that the sample stays bounded
-    s32 = np.nan_to_num(s, nan=0.0).astype(np.float32)
-    t1 = time.perf_counter()
-    sel = orc.select_passing(s32, bs, w.l_pass)
-    kp, vp = orc.gather_prefix(x.f32("k_anchor"), x.f32("v_anchor"), kc, vc, sel)
-    t_sel = time.perf_counter() - t1
-    G = w.hq // w.hkv
-    order = [g * G + j for j in range(G) for g in range(w.hkv)]   # one head per group first
-    L = int(bs[v + 1] - bs[v])
-    rows = np.arange(bs[v], bs[v + 1])
-    heads = []
-    t2 = time.perf_counter()
-    for h in order:                        # add heads until about budget_s of CPU work
-        orc.attend(x.f32("q_ctx"), kp, vp, kc, vc, bs, w.l_anchor, w.l_pass, w.hq, w.hkv,
-                   scale, rows=rows, heads=[h])
-        heads.append(h)
-        if time.perf_counter() - t2 >= budget_s:
-            break
-    t_attn = time.perf_counter() - t2
-    P = w.l_anchor + v * w.l_pass
-    sample_pairs = (L * P + L * (L + 1) // 2) * len(heads)
-    total_pairs = attention_flops(bs, w.l_anchor, w.l_pass, 1, 1) / 4
-    est = t_score * n + t_sel + t_attn * (total_pairs / sample_pairs)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        cores = len(os.sched_getaffinity(0))
-    return {"value": x.N / est, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"float64 numpy oracle on block {v} of {n}: scores+selection for all "
-                       f"{w.hkv} KV heads ({t_score:.1f}s), gather ({t_sel:.1f}s), attention of "
-                       f"{len(heads)} of {w.hq} heads over the block's {L} rows ({t_attn:.1f}s); "
-                       f"layer time extrapolated by block count (scores) and by visible "
-                       f"(row, key) pairs (attention): {est:.0f}s per layer")}
+    bs = np.asarray(x.block_starts, np.int64)
+    n, G, d = len(bs) - 1, w.hq // w.hkv, w.head_dim
+    scale = 1.0 / math.sqrt(d)
+    host_cpus = len(os.sched_getaffinity(0))
+    workers = workers or max(1, min(MAX_POOL_WORKERS, host_cpus))
+    qq, kc, vc = x.bits["q_query"], x.bits["k_ctx"], x.bits["v_ctx"]
+    qc = x.bits["q_ctx"]
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(workers, mp_context=ctx,
+                                                initializer=_pool_init) as pool:
+        # warm the workers (imports) outside the timed parts
+        list(pool.map(_warm, range(4 * workers)))
+        score_tasks = [dict(v=v, g=g, scale=scale, q_query=qq[:, g * G:(g + 1) * G],
+                            k_block=kc[bs[v]:bs[v + 1], g:g + 1])
+                       for v in range(n) for g in range(w.hkv)]
+        t0 = time.perf_counter()
+        res = list(pool.map(_oracle_score_task, score_tasks))
+        t_score_wall = time.perf_counter() - t0
+        s = np.full((w.hkv, x.N), np.nan)
+        cpu_score = 0.0
+        for v, g, sv, dt in res:
+            s[g, bs[v]:bs[v + 1]] = sv
+            cpu_score += dt
+        t1 = time.perf_counter()
+        sel = orc.select_passing(s.astype(np.float32), bs, w.l_pass)
+        kp, vp = orc.gather_prefix(x.f32("k_anchor"), x.f32("v_anchor"), x.f32("k_ctx"),
+                                   x.f32("v_ctx"), sel)
+        t_sel_gather = time.perf_counter() - t1
+        from synthetic import bf16_bits
+        kp_bits, vp_bits = bf16_bits(kp.astype(np.float32)), bf16_bits(vp.astype(np.float32))
+        rng = np.random.default_rng(seed)
+        attn_tasks, sample_pairs, sampled = [], 0, []
+        for v in range(n):
+            L = int(bs[v + 1] - bs[v])
+            T = (L + 255) // 256
+            if tiles_per_unit is None:
+                tiles = [(0, L)]
+            else:
+                pick = sorted(rng.choice(T, size=min(T, tiles_per_unit), replace=False))
+                tiles = [(256 * t, min(L, 256 * t + 256)) for t in pick]
+            P = w.l_anchor + v * w.l_pass
+            sampled += [(v, a, b) for a, b in tiles]
+            for g in range(w.hkv):
+                for a, b in tiles:
+                    lo = int(bs[v])
+                    attn_tasks.append(dict(
+                        scale=scale, rows=(a, b),
+                        q_rows=qc[lo:lo + b, g * G:(g + 1) * G],
+                        k_pre=kp_bits[g:g + 1, :P], v_pre=vp_bits[g:g + 1, :P],
+                        k_loc=kc[lo:lo + b, g:g + 1], v_loc=vc[lo:lo + b, g:g + 1]))
+                    sample_pairs += visible_pairs(bs, w.l_anchor, w.l_pass, v, a, b) * G
+        t2 = time.perf_counter()
+        cpu_attn = sum(pool.map(_oracle_attn_task, attn_tasks))
+        t_attn_wall = time.perf_counter() - t2
+    total_pairs = sum(visible_pairs(bs, w.l_anchor, w.l_pass, v, 0, int(bs[v + 1] - bs[v]))
+                      for v in range(n)) * w.hq
+    ratio = total_pairs / sample_pairs
+    est = t_sel_gather + (cpu_score + cpu_attn * ratio) / workers
+    raw = dict(cpu_score_s=cpu_score, cpu_attn_sample_s=cpu_attn, sel_gather_s=t_sel_gather,
+               score_wall_s=t_score_wall, attn_wall_s=t_attn_wall, sample_pairs=sample_pairs,
+               total_pairs=total_pairs, workers=workers, layer_s=est, tiles=sampled)
+    what = ("every row" if tiles_per_unit is None
+            else f"{tiles_per_unit} seeded 256-row tiles of each (block, KV head) unit")
+    rec = {"value": x.N / est, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+           "host_cpus": host_cpus, "blas_threads_per_worker": 1,
+           "sample": (f"float64 numpy oracle in a pool of {workers} single-threaded worker "
+                      f"processes over the {n} x {w.hkv} (block, KV head) units: scores of "
+                      f"every unit ({cpu_score:.1f} core-s), selection + gather in the parent "
+                      f"({t_sel_gather:.1f} s), attention of all {G} heads of each unit on "
+                      f"{what}: {sample_pairs:.3e} of {total_pairs:.3e} visible (row, key) "
+                      f"pairs ({cpu_attn:.1f} core-s, {t_attn_wall:.1f} s wall); layer time = "
+                      f"selection + gather + (scores + attention x {ratio:.1f}) / {workers} "
+                      f"workers = {est:.0f} s")}
+    return rec, raw
 
 
 def main():
@@ -344,7 +436,7 @@ def main():
     }
     if not (args.profile or args.no_cpu_baseline):
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(x)
+        rec["cpu_baseline"], _ = cpu_baseline(x)
     print(json.dumps(rec), flush=True)
 
 

@@ -108,14 +108,20 @@ apbv_status apbv_score_select(const apbv_layout* layout, const apbv_bf16* q_quer
  *
  *   k_anchor, v_anchor [l_anchor, hkv, d] bf16, contiguous (may be NULL if l_anchor == 0)
  *   k_ctx, v_ctx       [N, hkv, d] bf16 (kv_row_stride)
- *   sel                [n_blocks, hkv, l_pass] int32, every entry in [0, N)
+ *   sel                [n_blocks, hkv, l_pass] int32; every entry of sel[v] must be a row
+ *                      of block v, i.e. in [block_starts[v], block_starts[v+1])
  *   k_pre, v_pre       [hkv, l_anchor + n_blocks*l_pass, d] bf16 out
- * Out-of-range entries of sel are clamped into [0, N) rather than faulting.
+ *   sel_errors         device int32 counter, or NULL: the number of sel entries outside
+ *                      their own block is ADDED to it (the caller zeroes it beforehand and
+ *                      reads it after the stream has reached this call)
+ * An entry outside its block is an error of the caller; it is counted into sel_errors when
+ * one is given, and is clamped into its block (the first or last row) so that no read leaves
+ * the context: the prefix row it produces is then meaningless but memory stays safe.
  */
 apbv_status apbv_gather_passing(const apbv_layout* layout, const apbv_bf16* k_anchor,
                                 const apbv_bf16* v_anchor, const apbv_bf16* k_ctx,
                                 const apbv_bf16* v_ctx, const int32_t* sel, apbv_bf16* k_pre,
-                                apbv_bf16* v_pre, void* stream);
+                                apbv_bf16* v_pre, int32_t* sel_errors, void* stream);
 
 /*
  * Step 3: approximate attention of the context rows (same page and part: attention over

@@ -53,7 +53,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "apbv_score_select_workspace": (_I32, [_LP, ctypes.POINTER(_SZ)]),
             "apbv_score_select": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
-            "apbv_gather_passing": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+            "apbv_gather_passing": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
             "apbv_approx_attn_prefill": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
             "apbv_query_forward_workspace": (_I32, [_LP, ctypes.POINTER(_SZ)]),
             "apbv_query_forward": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -216,8 +216,10 @@ def score_select(layout: Layout, q_query, k_ctx, *, scores=None, sel=None, works
 
 
 def gather_passing(layout: Layout, k_anchor, v_anchor, k_ctx, v_ctx, sel, *, k_pre=None,
-                   v_pre=None):
-    """Step 2 (anchor + passing prefix per KV head). Returns (k_pre, v_pre)."""
+                   v_pre=None, sel_errors=None):
+    """Step 2 (anchor + passing prefix per KV head). Returns (k_pre, v_pre). ``sel_errors``
+    (an int32 tensor of one element, zeroed by the caller) receives the count of ``sel``
+    entries outside their own block."""
     import torch
     shape = (layout.hkv, layout.pre_rows, layout.head_dim)
     if k_pre is None:
@@ -233,7 +235,8 @@ def gather_passing(layout: Layout, k_anchor, v_anchor, k_ctx, v_ctx, sel, *, k_p
         _arg(v_ctx, "v_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
         _arg(sel, "sel", torch.int32, L.n_blocks, L.hkv * L.l_pass),
         _arg(k_pre, "k_pre", bf, L.hkv, L.pre_rows * d),
-        _arg(v_pre, "v_pre", bf, L.hkv, L.pre_rows * d))
+        _arg(v_pre, "v_pre", bf, L.hkv, L.pre_rows * d),
+        _arg(sel_errors, "sel_errors", torch.int32, 1, 1, required=False))
     _check(lib().apbv_gather_passing(L.ref(), *args, _stream(k_ctx.device)),
            "apbv_gather_passing")
     return k_pre, v_pre

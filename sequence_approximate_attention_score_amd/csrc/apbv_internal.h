@@ -145,9 +145,11 @@ struct GatherParams {
   const int32_t* sel;
   uint16_t* kpre;
   uint16_t* vpre;
+  int32_t* sel_errors;   // count of sel entries outside their own block, or null
   int64_t kv_stride;
   int32_t hkv, l_anchor, l_pass, n_blocks, pre_rows, n_tokens;
   int32_t row_begin, row_count;   // prefix rows written by one launch
+  int32_t bs[APBV_MAX_BLOCKS + 1];
 };
 
 hipError_t launch_gather(const GatherParams& p, int head_dim, hipStream_t stream);

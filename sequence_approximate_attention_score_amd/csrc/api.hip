@@ -166,9 +166,10 @@ apbv_status score_params(const apbv_layout* layout, const Checked& c, const apbv
 }
 
 // Checks of the gather call and its parameters for prefix rows [row_begin, row_begin + count).
-apbv_status gather_params(const Checked& c, const apbv_bf16* k_anchor, const apbv_bf16* v_anchor,
-                          const apbv_bf16* k_ctx, const apbv_bf16* v_ctx, const int32_t* sel,
-                          apbv_bf16* k_pre, apbv_bf16* v_pre, GatherParams& p) {
+apbv_status gather_params(const apbv_layout* layout, const Checked& c, const apbv_bf16* k_anchor,
+                          const apbv_bf16* v_anchor, const apbv_bf16* k_ctx,
+                          const apbv_bf16* v_ctx, const int32_t* sel, apbv_bf16* k_pre,
+                          apbv_bf16* v_pre, int32_t* sel_errors, GatherParams& p) {
   APBV_TRY(check_ptr(k_anchor, "k_anchor", c.l_a > 0));
   APBV_TRY(check_ptr(v_anchor, "v_anchor", c.l_a > 0));
   APBV_TRY(check_ptr(k_ctx, "k_ctx", c.l_p > 0));
@@ -176,7 +177,11 @@ apbv_status gather_params(const Checked& c, const apbv_bf16* k_anchor, const apb
   APBV_TRY(check_ptr(sel, "sel", c.l_p > 0));
   APBV_TRY(check_ptr(k_pre, "k_pre", c.pre_rows > 0));
   APBV_TRY(check_ptr(v_pre, "v_pre", c.pre_rows > 0));
+  if (sel_errors != nullptr && ((uintptr_t)sel_errors & 3u) != 0)
+    return fail(APBV_EINVAL, "sel_errors is not 4-byte aligned");
   memset(&p, 0, sizeof(p));
+  p.sel_errors = sel_errors;
+  for (int v = 0; v <= c.n; ++v) p.bs[v] = layout->block_starts[v];
   p.ka = k_anchor;
   p.va = v_anchor;
   p.kc = k_ctx;
@@ -321,11 +326,12 @@ apbv_status apbv_score_select(const apbv_layout* layout, const apbv_bf16* q_quer
 apbv_status apbv_gather_passing(const apbv_layout* layout, const apbv_bf16* k_anchor,
                                 const apbv_bf16* v_anchor, const apbv_bf16* k_ctx,
                                 const apbv_bf16* v_ctx, const int32_t* sel, apbv_bf16* k_pre,
-                                apbv_bf16* v_pre, void* stream) {
+                                apbv_bf16* v_pre, int32_t* sel_errors, void* stream) {
   Checked c;
   APBV_TRY(check_layout(layout, c));
   GatherParams p;
-  APBV_TRY(gather_params(c, k_anchor, v_anchor, k_ctx, v_ctx, sel, k_pre, v_pre, p));
+  APBV_TRY(gather_params(layout, c, k_anchor, v_anchor, k_ctx, v_ctx, sel, k_pre, v_pre,
+                         sel_errors, p));
   const hipError_t e = launch_gather(p, c.d, (hipStream_t)stream);
   if (e != hipSuccess) return fail(APBV_EHIP, "gather launch: %s", hipGetErrorString(e));
   g_err[0] = 0;
@@ -405,7 +411,8 @@ apbv_status apbv_prefill_layer(const apbv_layout* layout, const apbv_bf16* q_que
   ScoreParams sp;
   APBV_TRY(score_params(layout, c, q_query, k_ctx, scores, sel, workspace, workspace_bytes, sp));
   GatherParams gp;
-  APBV_TRY(gather_params(c, k_anchor, v_anchor, k_ctx, v_ctx, sel, k_pre, v_pre, gp));
+  APBV_TRY(gather_params(layout, c, k_anchor, v_anchor, k_ctx, v_ctx, sel, k_pre, v_pre,
+                         nullptr, gp));
   AttnParams ap;
   APBV_TRY(attn_params(layout, c, q_ctx, k_pre, v_pre, k_ctx, v_ctx, out, lse, ap));
   const int nb = ap.sched.n_buckets();

@@ -35,7 +35,13 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherParams p) 
     const int r = row - p.l_anchor;
     const int v = r / p.l_pass, k = r % p.l_pass;
     int j = p.sel[((int64_t)v * p.hkv + g) * p.l_pass + k];
-    j = j < 0 ? 0 : (j >= p.n_tokens ? p.n_tokens - 1 : j);
+    // an entry outside its own block is a caller error: counted (once per entry) when a
+    // counter is given, and clamped into the block so that no read leaves the context
+    const int lo = p.bs[v], hi = p.bs[v + 1];
+    if (j < lo || j >= hi) {
+      if (p.sel_errors != nullptr && tensor == 0 && ch == 0) atomicAdd(p.sel_errors, 1);
+      j = j < lo ? lo : hi - 1;
+    }
     const uint16_t* c = tensor == 0 ? p.kc : p.vc;
     src = c + (int64_t)j * p.kv_stride + g * D;
   }

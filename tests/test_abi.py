@@ -86,8 +86,13 @@ def test_invalid_pointers_and_ranges():
     big = small_layout(l_query=12000)            # 2 * 12000 score rows exceed the LDS budget
     st = L.apbv_score_select(big.ref(), 0x1000, 0x2000, None, 0x3000, 0x10000, 1 << 30, None)
     assert st == _lib.APBV_EUNSUPPORTED
-    st = L.apbv_gather_passing(lay.ref(), 0x1000, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None)
+    st = L.apbv_gather_passing(lay.ref(), 0x1000, None, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000,
+                               None, None)
     assert st == _lib.APBV_EINVAL                                   # v_anchor missing
+    st = L.apbv_gather_passing(lay.ref(), 0x1000, 0x1100, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000,
+                               0x7002, None)
+    assert st == _lib.APBV_EINVAL                                   # sel_errors misaligned
+    assert "sel_errors" in L.apbv_last_error().decode()
     assert L.apbv_approx_attn_prefill(None, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == _lib.APBV_EINVAL
     assert L.apbv_status_str(3).decode().startswith("workspace")
 

@@ -402,3 +402,38 @@ def test_layer_call_stays_in_bounds():
     assert np.array_equal(v["scores"].cpu().numpy(), g["scores"])
     assert np.array_equal(host_f64(v["out"]), g["out"])
     say("  guards intact around every output of the one-call layer")
+
+
+def test_gather_counts_selections_outside_their_block():
+    """Entries of sel outside their own block are counted into sel_errors and clamped into the
+    block (its first or last row); every other prefix row is the oracle's gather."""
+    x = generate(dataclasses.replace(workload("c0"), name="selerr", keys="iid", hq=4, hkv=2,
+                                     head_dim=128, total_tokens=900, n_blocks=3, block_len=300,
+                                     l_anchor=16, l_query=8, l_pass=20))
+    lay = layout_of(x)
+    d = upload(x)
+    _, sel = apbv.score_select(lay, d["q_query"], d["k_ctx"])
+    torch.cuda.synchronize()
+    bad = sel.cpu().numpy().copy()
+    bs = x.block_starts
+    bad[0, 0, 0] = bs[1]          # a row of the next block
+    bad[1, 1, 5] = -5             # before the context
+    bad[2, 0, 19] = x.N + 10      # past the context
+    bad[1, 0, 0] = bs[1] - 1      # the last row of the previous block
+    errs = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kp, vp = apbv.gather_passing(lay, d["k_anchor"], d["v_anchor"], d["k_ctx"], d["v_ctx"],
+                                 torch.from_numpy(bad).cuda(), sel_errors=errs)
+    torch.cuda.synchronize()
+    assert int(errs.item()) == 4
+    fixed = bad.copy()
+    for v in range(lay.n_blocks):
+        fixed[v] = np.clip(fixed[v], bs[v], bs[v + 1] - 1)
+    ka, va = x.f32("k_anchor"), x.f32("v_anchor")
+    k_or, v_or = orc.gather_prefix(ka, va, x.f32("k_ctx"), x.f32("v_ctx"), fixed)
+    assert np.array_equal(host_f64(kp), k_or) and np.array_equal(host_f64(vp), v_or)
+    # a valid selection adds nothing to the counter
+    apbv.gather_passing(lay, d["k_anchor"], d["v_anchor"], d["k_ctx"], d["v_ctx"], sel,
+                        sel_errors=errs)
+    torch.cuda.synchronize()
+    assert int(errs.item()) == 4
+    say("  out-of-block selections counted (4) and clamped into their blocks")
