@@ -137,3 +137,36 @@ def test_layer_split_on_random_layouts(seed):
     got = dict(out=out, lse=lse, sel=sel, scores=scores, k_pre=k_pre, v_pre=v_pre)
     for k in ("scores", "sel", "k_pre", "v_pre", "out", "lse"):
         assert torch.equal(ref[k], got[k]), (seed, k)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["c0", "ragged_odd_n", "zigzag_off", "64k"])
+def test_layer_matches_oracle(name):
+    """The one-call layer with its second stream, against the oracle (not only against the
+    three calls): every block's scores and selection, the prefix bitwise, and every row of
+    one query head per KV group. Small layouts get a CU count that makes the plan split the
+    attention into two launches around the second stream's selections."""
+    from fullsize import fullsize_check
+    wl, over, bs, lay_over = CASES[name]
+    x = generate(workload(wl, **over))
+    lay = layout_of(x, block_starts=bs, **lay_over)
+    nb = apbv.num_buckets(lay)
+    cus = 0
+    if wl == "c0" and nb > 1 and lay.l_pass > 0 and lay.c.zigzag:
+        cus = apbv.schedule(lay, nb // 2, nb).shape[0] * lay.hq
+    late, early = _lib.prefill_layer_plan(
+        lay, cus or torch.cuda.get_device_properties(0).multi_processor_count)
+    say(f"layer {name}: buckets={nb} late buckets from {late}, early blocks {early}")
+
+    def runner(lay, d):
+        shape = (lay.hkv, lay.pre_rows, lay.head_dim)
+        k_pre = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        v_pre = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        out, lse, sel, scores = apbv.prefill_layer(
+            lay, d["q_query"], d["q_ctx"], d["k_ctx"], d["v_ctx"], d["k_anchor"], d["v_anchor"],
+            aux_stream=torch.cuda.Stream(), k_pre=k_pre, v_pre=v_pre, want_scores=True,
+            want_lse=True, compute_units=cus)
+        return scores, sel, k_pre, v_pre, out, lse
+
+    heads = list(range(lay.hq)) if wl == "c0" else None
+    fullsize_check(x, lay, all_rows=True, heads=heads, runner=runner)

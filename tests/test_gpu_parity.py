@@ -1,11 +1,9 @@
 """HIP path against the oracle, through the C ABI, on seeded synthetic inputs (needs a GPU).
 
-Small cases compare every element; the full-size workloads (64K-256K tokens, the launch
-configuration the benchmark times) compare sampled blocks (scores and selection, computed
-whole by the oracle) and sampled rows (attention, computed row by row by the oracle).
-Attention is teacher-forced: the oracle's attention runs on the prefix gathered from the
-GPU's own selection, so a near-tie difference in selection cannot leak into the attention
-comparison; where the two selections agree the end-to-end outputs are compared too.
+Small cases, every element. Attention is teacher-forced: the oracle's attention runs on the
+prefix gathered from the GPU's own selection, so a near-tie difference in selection cannot
+leak into the attention comparison; where the two selections agree the end-to-end outputs
+are compared too. The full-size workloads are in test_gpu_fullsize.py.
 """
 from __future__ import annotations
 
@@ -267,68 +265,6 @@ def test_zigzag_ranges_and_determinism():
                                  range_begin=bkt, range_end=bkt + 1)
     torch.cuda.synchronize()
     assert np.array_equal(host_f64(out), a["out"])
-
-
-# ------------------------------------------------------------------------- full size, sampled
-def sample_rows(bs, tile, rng, per_block=24):
-    rows = []
-    for v in range(len(bs) - 1):
-        lo, hi = int(bs[v]), int(bs[v + 1])
-        pick = {lo, lo + 1, hi - 1, hi - 2, min(lo + tile - 1, hi - 1), min(lo + tile, hi - 1)}
-        pick |= set(int(r) for r in rng.integers(lo, hi, per_block))
-        rows += sorted(pick)
-    return np.asarray(sorted(set(rows)))
-
-
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
-def test_full_size_sampled(name):
-    x = generate(workload(name))
-    w = x.w
-    lay = layout_of(x)
-    bs = x.block_starts
-    rng = np.random.default_rng(7)
-    rows = sample_rows(bs, apbv.attn_tile_rows(w.head_dim), rng)
-    heads = [0, w.hq // 2, w.hq - 1]
-    blocks = sorted({0, lay.n_blocks // 2, lay.n_blocks - 1})
-    full_check(x, lay, rows=rows, heads=heads, blocks=blocks)
-
-
-def test_dense_causal_128k_sampled():
-    """Dense causal attention over [anchor | 128K context] (n = 1, no prefix): the
-    comparison the frame-balanced 128K workload reports, on sampled rows."""
-    w = workload("c4")
-    x = generate(w)
-    N = x.N + w.l_anchor
-    lay = apbv.Layout([0, N], l_anchor=0, l_query=0, l_pass=0, hq=w.hq, hkv=w.hkv,
-                      head_dim=w.head_dim)
-    q = np.concatenate([x.bits["q_anchor"], x.bits["q_ctx"]])
-    k = np.concatenate([x.bits["k_anchor"], x.bits["k_ctx"]])
-    v = np.concatenate([x.bits["v_anchor"], x.bits["v_ctx"]])
-    dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
-    out, lse = apbv.approx_attn_prefill(lay, dq, None, None, dk, dv, want_lse=True)
-    torch.cuda.synchronize()
-    rows = np.asarray(sorted({0, 1, 127, 128, N - 1} | set(np.random.default_rng(3).integers(0, N, 40).tolist())))
-    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
-    o_or, l_or = orc.attend(f(q), np.zeros((w.hkv, 0, w.head_dim)), np.zeros((w.hkv, 0, w.head_dim)),
-                            f(k), f(v), [0, N], 0, 0, w.hq, w.hkv, 1 / math.sqrt(w.head_dim),
-                            rows=rows, heads=[0, 27])
-    check_attention(host_f64(out), o_or, "dense causal 128K")
-
-
-@pytest.mark.parametrize("name", ["buckets_2", "buckets_4", "buckets_6", "no_passing"])
-def test_sweep_128k_sampled(name):
-    """The bucket-count sweep (2, 4, 6 buckets over 128K tokens; 8 is the headline layout)
-    and the anchor-only baseline without passing blocks, on the same 128K context: sampled
-    blocks (scores, selection) and rows (attention, teacher-forced)."""
-    x = generate(workload("c2"))
-    lay_d = [l for l in sweep_layouts(x.w) if l["name"] == name][0]
-    lay = layout_of(x, block_starts=lay_d["block_starts"], l_anchor=lay_d["l_anchor"],
-                    l_pass=lay_d["l_pass"])
-    bs = lay_d["block_starts"]
-    rng = np.random.default_rng(11)
-    rows = sample_rows(bs, apbv.attn_tile_rows(x.w.head_dim), rng, per_block=12)
-    blocks = sorted({0, lay.n_blocks - 1})
-    full_check(x, lay, rows=rows, heads=[0, 13, 27], blocks=blocks)
 
 
 def _guarded(shape, dtype, fill):
