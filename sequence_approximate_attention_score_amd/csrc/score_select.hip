@@ -14,8 +14,9 @@
 //      each row's log-sum-exp, S = Q . K^T is recomputed on MFMA (one key per lane) and the
 //      probabilities are summed down the rows.
 //   3. selection: per (block, KV head) an exact radix select of the l_p-th largest score on
-//      order-preserving 32-bit keys, then a stable compaction (ties to the lower row) that
-//      writes the chosen rows in ascending order, placed by block-wide prefix sums.
+//      order-preserving 32-bit keys (kept in LDS), then a stable compaction (ties to the
+//      lower row) that writes the chosen rows in ascending order, placed by block-wide
+//      prefix sums.
 #include "apbv_device.h"
 #include "apbv_internal.h"
 
@@ -273,7 +274,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
-// Exclusive prefix sum over the workgroup's threads in thread order (wsum: 4 words of LDS).
+// Exclusive prefix sum over the workgroup's threads in thread order (wsum: one word of LDS
+// per wave).
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_incl_scan(x);
@@ -285,35 +287,51 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum) 
   return before + inc - x;
 }
 
-// One workgroup per (block, KV head).
-//  * Radix select on order-preserving 32-bit keys, 8 bits per pass from the top, finds the
-//    exact l_pass-th largest key T and how many keys equal to T are still needed. Each wave
-//    counts into its own histogram (less atomic contention); wave 0 sums them and finds the
-//    digit with one suffix scan over its lanes (lane l holds digits 4l .. 4l+3).
+// One workgroup of 1024 threads per (block, KV head). The block's scores are turned once
+// into order-preserving 32-bit keys, held in LDS when the block has at most kSelCache rows
+// (otherwise re-read from the score buffer by every pass).
+//  * Radix select, 8 bits per pass from the top, finds the exact l_pass-th largest key T and
+//    how many keys equal to T are still needed. Each wave counts into its own histogram (less
+//    atomic contention); wave 0 sums them and finds the digit with one suffix scan over its
+//    lanes (lane l holds digits 4l .. 4l+3).
 //  * Stable compaction in row order: thread t owns a contiguous run of rows. It counts its
 //    keys above T and equal to T; an exclusive scan of the equal counts gives how many tied
 //    rows come before its run (ties go to the lower rows), a second scan of the rows it
 //    keeps gives its output position.
-__global__ __launch_bounds__(kThreads) void select_topk(const ScoreParams p) {
-  __shared__ uint32_t hist[kThreads / 64][256];
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelCache = 16384;   // rows whose keys stay in LDS (64 KB)
+
+template <bool CACHED>
+__global__ __launch_bounds__(kSelThreads) void select_topk(const ScoreParams p) {
+  __shared__ uint32_t hist[kSelWaves][256];
+  __shared__ uint32_t keys[CACHED ? kSelCache : 1];
   __shared__ uint32_t sh_prefix, sh_need;
-  __shared__ uint32_t wsum[kThreads / 64];
+  __shared__ uint32_t wsum[kSelWaves];
 
   const int v = p.v_begin + blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
   const int lo = p.bs[v], hi = p.bs[v + 1];
-  const float* sc = p.scores + (int64_t)g * p.n_tokens;
+  const int L = hi - lo;
+  const float* sc = p.scores + (int64_t)g * p.n_tokens + lo;
   int32_t* out = p.sel + ((int64_t)v * p.hkv + g) * p.l_pass;
   if (p.l_pass == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto key = [&](int j) -> uint32_t {   // key of row lo + j
+    if constexpr (CACHED) return keys[j];
+    else return order_key(sc[j]);
+  };
+  if constexpr (CACHED) {
+    for (int j = tid; j < L; j += kSelThreads) keys[j] = order_key(sc[j]);
+  }
 
   uint32_t prefix = 0, need = (uint32_t)p.l_pass;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-    for (int i = tid; i < (kThreads / 64) * 256; i += kThreads) (&hist[0][0])[i] = 0;
+    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int j = lo + tid; j < hi; j += kThreads) {
-      const uint32_t k = order_key(sc[j]);
+    for (int j = tid; j < L; j += kSelThreads) {
+      const uint32_t k = key(j);
       if ((k & hmask) == (prefix & hmask)) atomicAdd(&hist[wave][(k >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -323,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void select_topk(const ScoreParams p) {
       for (int e = 0; e < 4; ++e) {
         b[e] = 0;
 #pragma unroll
-        for (int w = 0; w < kThreads / 64; ++w) b[e] += hist[w][4 * lane + e];
+        for (int w = 0; w < kSelWaves; ++w) b[e] += hist[w][4 * lane + e];
         s += b[e];
       }
       const uint32_t incl = wave_incl_scan(s);
@@ -347,12 +365,11 @@ __global__ __launch_bounds__(kThreads) void select_topk(const ScoreParams p) {
   }
 
   const uint32_t T = prefix;
-  const int L = hi - lo;
-  const int run = (L + kThreads - 1) / kThreads;
-  const int r0 = lo + min(tid * run, L), r1 = lo + min((tid + 1) * run, L);
+  const int run = (L + kSelThreads - 1) / kSelThreads;
+  const int r0 = min(tid * run, L), r1 = min((tid + 1) * run, L);
   uint32_t n_gt = 0, n_eq = 0;
   for (int j = r0; j < r1; ++j) {
-    const uint32_t k = order_key(sc[j]);
+    const uint32_t k = key(j);
     n_gt += k > T;
     n_eq += k == T;
   }
@@ -361,11 +378,11 @@ __global__ __launch_bounds__(kThreads) void select_topk(const ScoreParams p) {
   uint32_t pos = block_excl_scan(n_gt + eq_take, wsum);
   uint32_t eq_seen = 0;
   for (int j = r0; j < r1; ++j) {
-    const uint32_t k = order_key(sc[j]);
+    const uint32_t k = key(j);
     if (k > T) {
-      out[pos++] = j;
+      out[pos++] = lo + j;
     } else if (k == T) {
-      if (eq_seen < eq_take) out[pos++] = j;
+      if (eq_seen < eq_take) out[pos++] = lo + j;
       ++eq_seen;
     }
   }
@@ -412,7 +429,12 @@ hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block
     if (e != hipSuccess) return e;
   }
   if (p.l_pass > 0) {
-    hipLaunchKernelGGL(select_topk, dim3(p.v_count * p.hkv), dim3(kThreads), 0, stream, p);
+    if (max_block <= kSelCache)
+      hipLaunchKernelGGL(select_topk<true>, dim3(p.v_count * p.hkv), dim3(kSelThreads), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL(select_topk<false>, dim3(p.v_count * p.hkv), dim3(kSelThreads), 0,
+                         stream, p);
     return hipGetLastError();
   }
   return hipSuccess;
