@@ -36,7 +36,8 @@
  *    calling thread). A failed launch returns APBV_EHIP (apbv_prefill_layer may have
  *    enqueued its earlier launches by then).
  *  - Calls on one stream may be issued from several threads; the library keeps no mutable
- *    global state apart from the per-thread error message.
+ *    global state apart from the per-thread error message, and the per-device scratch of
+ *    apbv_score_select_noalloc (with its address, looked up once per device).
  */
 #ifndef APBV_H
 #define APBV_H
@@ -99,6 +100,24 @@ apbv_status apbv_score_select_workspace(const apbv_layout* layout, size_t* bytes
 apbv_status apbv_score_select(const apbv_layout* layout, const apbv_bf16* q_query,
                               const apbv_bf16* k_ctx, float* scores, int32_t* sel,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Step 1 without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same kernels and
+ * results as apbv_score_select; the workspace is a 16 MiB scratch array inside the library,
+ * one per device, held until the process ends. Nothing is allocated or freed by the call.
+ *
+ *   q_query, k_ctx, scores, sel, stream: as apbv_score_select (stream must belong to the
+ *   calling thread's current device, whose scratch is used)
+ * A layout needing more than 16 MiB (apbv_score_select_workspace() with scores given, or
+ * with scores NULL when they are kept in the scratch) returns APBV_EUNSUPPORTED before
+ * anything is enqueued. The scratch keeps the last call's contents (every call writes what
+ * it reads); calls that overlap in time on one device (several streams or threads) race on
+ * it and must be ordered by the caller.
+ */
+apbv_status apbv_score_select_noalloc(const apbv_layout* layout, const apbv_bf16* q_query,
+                                      const apbv_bf16* k_ctx, float* scores, int32_t* sel,
+                                      void* stream);
 
 /*
  * Step 2: collect anchor and passing blocks (same page and part: every host gathers the

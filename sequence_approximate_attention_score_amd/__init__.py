@@ -11,12 +11,13 @@ merged through their lse). This package is the thin Python binding over that lib
 """
 from ._lib import (ApbvError, Layout, approx_attn_prefill, attn_tile_rows, gather_passing,
                    lib, num_buckets, prefill_layer, prefill_layer_plan, query_forward,
-                   query_forward_workspace, schedule, score_select, score_select_workspace,
-                   version)
+                   query_forward_workspace, schedule, score_select, score_select_noalloc,
+                   score_select_workspace, version)
 
 __all__ = ["ApbvError", "Layout", "approx_attn_prefill", "attn_tile_rows", "gather_passing",
            "lib", "num_buckets", "prefill_layer", "prefill_layer_plan", "query_forward",
-           "query_forward_workspace", "schedule", "score_select", "score_select_workspace",
+           "query_forward_workspace", "schedule", "score_select", "score_select_noalloc",
+           "score_select_workspace",
            "version", "run_layer"]
 
 

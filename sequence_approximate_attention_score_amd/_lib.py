@@ -21,7 +21,8 @@ MAX_BLOCKS = 64
 EXPORTED = ["apbv_score_select_workspace", "apbv_score_select", "apbv_gather_passing",
             "apbv_approx_attn_prefill", "apbv_query_forward_workspace", "apbv_query_forward",
             "apbv_num_buckets", "apbv_schedule", "apbv_attn_tile_rows", "apbv_status_str",
-            "apbv_last_error", "apbv_version", "apbv_prefill_layer", "apbv_prefill_layer_plan"]
+            "apbv_last_error", "apbv_version", "apbv_prefill_layer", "apbv_prefill_layer_plan",
+            "apbv_score_select_noalloc"]
 
 
 class ApbvError(RuntimeError):
@@ -53,6 +54,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "apbv_score_select_workspace": (_I32, [_LP, ctypes.POINTER(_SZ)]),
             "apbv_score_select": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+            "apbv_score_select_noalloc": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP]),
             "apbv_gather_passing": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
             "apbv_approx_attn_prefill": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
             "apbv_query_forward_workspace": (_I32, [_LP, ctypes.POINTER(_SZ)]),
@@ -212,6 +214,28 @@ def score_select(layout: Layout, q_query, k_ctx, *, scores=None, sel=None, works
         _arg(workspace, "workspace", torch.uint8, workspace.numel(), 1))
     _check(lib().apbv_score_select(L.ref(), *args, workspace.numel(), _stream(dev)),
            "apbv_score_select")
+    return scores, sel
+
+
+def score_select_noalloc(layout: Layout, q_query, k_ctx, *, scores=None, sel=None,
+                         want_scores: bool = True):
+    """Step 1 through the allocation-free entry point (the library's per-device scratch in
+    place of a workspace). Returns (scores or None, sel)."""
+    import torch
+    dev = k_ctx.device
+    if want_scores and scores is None:
+        scores = torch.empty((layout.hkv, layout.n_tokens), dtype=torch.float32, device=dev)
+    if sel is None:
+        sel = torch.empty((layout.n_blocks, layout.hkv, layout.l_pass), dtype=torch.int32, device=dev)
+    L, d = layout, layout.head_dim
+    bf, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    args = _pointers(
+        _arg(q_query, "q_query", bf, L.l_query, L.hq * d, required=L.l_query > 0),
+        _arg(k_ctx, "k_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(scores, "scores", f32, L.hkv, L.n_tokens, required=False),
+        _arg(sel, "sel", i32, L.n_blocks, L.hkv * L.l_pass))
+    _check(lib().apbv_score_select_noalloc(L.ref(), *args, _stream(dev)),
+           "apbv_score_select_noalloc")
     return scores, sel
 
 

@@ -5,7 +5,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "apbv_internal.h"
+
+// Scratch of the allocation-free scoring entry point (apbv_score_select_noalloc): the split
+// statistics and, when the caller passes no score buffer, the scores. The runtime gives every
+// device the library runs on its own copy, held until the process ends. In host code this
+// name is only a stand-in for the symbol: its device address comes from hipGetSymbolAddress
+// (scratch_of_current_device below) and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[16u << 20];
 
 namespace apbv {
 
@@ -96,6 +105,33 @@ apbv_status check_ptr(const void* p, const char* name, bool needed) {
   } while (0)
 
 int n_split_of(const Checked& c) { return (c.max_block + kScoreSplit - 1) / kScoreSplit; }
+
+constexpr size_t kScratchBytes = sizeof(scratch);
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch`, per device
+
+// Device address of the scratch array on the calling thread's current device, looked up
+// once per device with that device current.
+apbv_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(APBV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(APBV_EUNSUPPORTED, "device %d: the scratch supports devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(APBV_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return APBV_OK;
+}
 
 }  // namespace
 
@@ -317,6 +353,27 @@ apbv_status apbv_score_select(const apbv_layout* layout, const apbv_bf16* q_quer
   APBV_TRY(check_layout(layout, c));
   ScoreParams p;
   APBV_TRY(score_params(layout, c, q_query, k_ctx, scores, sel, workspace, workspace_bytes, p));
+  const hipError_t e = launch_score_select(p, c.d, c.max_block, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(APBV_EHIP, "score/select launch: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_score_select_noalloc(const apbv_layout* layout, const apbv_bf16* q_query,
+                                      const apbv_bf16* k_ctx, float* scores, int32_t* sel,
+                                      void* stream) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  const size_t need =
+      score_workspace_bytes(c.n, c.hkv, c.G * c.l_q, n_split_of(c), c.N, scores == nullptr);
+  if (need > kScratchBytes)
+    return fail(APBV_EUNSUPPORTED,
+                "this layout needs %zu bytes of scratch, the allocation-free entry point has "
+                "%zu (use apbv_score_select with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  APBV_TRY(scratch_of_current_device(&ws));
+  ScoreParams p;
+  APBV_TRY(score_params(layout, c, q_query, k_ctx, scores, sel, ws, kScratchBytes, p));
   const hipError_t e = launch_score_select(p, c.d, c.max_block, (hipStream_t)stream);
   if (e != hipSuccess) return fail(APBV_EHIP, "score/select launch: %s", hipGetErrorString(e));
   g_err[0] = 0;

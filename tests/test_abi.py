@@ -357,3 +357,18 @@ def test_layer_call_rejects_bad_stream_arguments_before_launch():
     assert call(0xA000, 0xB000, 0xC000, out=0x6008) == _lib.APBV_EINVAL   # misaligned out
     assert call(0xA000, 0xB000, 0xC000, ws=None) == _lib.APBV_EWORKSPACE
     assert call(0xA000, 0xB000, 0xC000, cus=-1) == _lib.APBV_EINVAL
+
+
+def test_noalloc_scoring_rejects_layouts_beyond_its_scratch_before_launch():
+    """The allocation-free scoring entry point refuses a layout whose workspace exceeds its
+    16 MiB scratch, on the host, before any GPU call."""
+    L = apbv.lib()
+    # 64 blocks x 8 KV heads x 16000 score rows of split statistics: about 65 MB
+    big = apbv.Layout(list(range(0, 64 * 2048 + 1, 2048)), l_anchor=0, l_query=2000, l_pass=16,
+                      hq=64, hkv=8, head_dim=128)
+    st = L.apbv_score_select_noalloc(big.ref(), 0x1000, 0x2000, None, 0x3000, None)
+    assert st == _lib.APBV_EUNSUPPORTED
+    assert "scratch" in L.apbv_last_error().decode()
+    ws = ctypes.c_size_t(0)
+    assert L.apbv_score_select_workspace(big.ref(), ctypes.byref(ws)) == 0
+    assert ws.value > 16 << 20
