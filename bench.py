@@ -10,11 +10,15 @@ layer (prefill_layer) on one stream and with the selection of later blocks on a 
 stream beside the attention, and one layer for each layout of the bucket sweep (2, 4, 6, 8
 buckets) and of the anchor-only baseline.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
-                    [--profile] [--calib-copy]
+Beside them, one layer of each other workload (64K, 256K and the variable-frame 128K
+layout, the last with dense causal attention over all of its tokens for comparison).
 
-``--profile`` shortens the run for rocprofv3 (no CPU baseline); ``--calib-copy`` also runs
-a plain 1 GiB device copy so that HBM byte counters can be scaled against a known size.
+    python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+                    [--profile] [--calib-copy] [--other-workloads c1,c3,c4]
+
+``--profile`` shortens the run for rocprofv3 (no CPU baseline, no other workloads);
+``--calib-copy`` also runs a plain 1 GiB device copy so that HBM byte counters can be scaled
+against a known size.
 """
 from __future__ import annotations
 
@@ -242,6 +246,80 @@ def cpu_baseline(x, tiles_per_unit: int | None = 2, workers: int | None = None, 
     return rec, raw
 
 
+def other_workload(name: str, dev, reps: int = 5) -> dict:
+    """One layer (score_select -> gather_passing -> approx_attn_prefill) of another workload:
+    median step and attention times over ``reps`` steps, tokens/s and the attention's fraction
+    of the bf16 peak. For the variable-frame 128K workload, dense causal attention over
+    [anchor | context] (one block, no prefix) is timed beside it."""
+    import torch
+    import sequence_approximate_attention_score_amd as apbv
+    from synthetic import generate, workload
+    w = workload(name)
+    print(f"# generating {w.name}: {w.description}", file=sys.stderr, flush=True)
+    x = generate(w)
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    d = {n: up(x.bits[n]) for n in ("q_query", "q_ctx", "k_ctx", "v_ctx", "k_anchor",
+                                    "v_anchor")}
+    lay = apbv.Layout(x.block_starts, l_anchor=w.l_anchor, l_query=w.l_query, l_pass=w.l_pass,
+                      hq=w.hq, hkv=w.hkv, head_dim=w.head_dim, zigzag=True)
+    ws = torch.empty(max(apbv.score_select_workspace(lay), 256), dtype=torch.uint8, device=dev)
+    sel = torch.empty((lay.n_blocks, w.hkv, w.l_pass), dtype=torch.int32, device=dev)
+    kp = torch.empty((w.hkv, lay.pre_rows, w.head_dim), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    out = torch.empty((x.N, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
+
+    def select_gather():
+        apbv.score_select(lay, d["q_query"], d["k_ctx"], sel=sel, workspace=ws,
+                          want_scores=False)
+        apbv.gather_passing(lay, d["k_anchor"], d["v_anchor"], d["k_ctx"], d["v_ctx"], sel,
+                            k_pre=kp, v_pre=vp)
+
+    def attend():
+        apbv.approx_attn_prefill(lay, d["q_ctx"], kp, vp, d["k_ctx"], d["v_ctx"], out=out)
+
+    def layer():
+        select_gather()
+        attend()
+
+    layer()
+    torch.cuda.synchronize()
+    layer_ms = median_ms(layer, reps)
+    attn_ms = median_ms(attend, reps)
+    fl = attention_flops(x.block_starts, w.l_anchor, w.l_pass, w.hq, w.head_dim)
+    rec = {"workload": f"{w.name}: {w.description}", "tokens": x.N,
+           "virtual_blocks": lay.n_blocks, "zigzag_buckets": apbv.num_buckets(lay),
+           "layer_ms": layer_ms, "tokens_per_s": x.N / (layer_ms * 1e-3),
+           "attention_ms": attn_ms, "attention_tflops": fl / (attn_ms * 1e-3) / 1e12,
+           "attention_frac_of_peak": fl / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    if w.frame_range:
+        # dense causal attention over [anchor | context]: one block, no prefix
+        del ws, sel, kp, vp
+        n_all = x.N + w.l_anchor
+        dense = apbv.Layout([0, n_all], l_anchor=0, l_query=0, l_pass=0, hq=w.hq, hkv=w.hkv,
+                            head_dim=w.head_dim)
+        qa = torch.cat([up(x.bits["q_anchor"]), d["q_ctx"]])
+        ka = torch.cat([d["k_anchor"], d["k_ctx"]])
+        va = torch.cat([d["v_anchor"], d["v_ctx"]])
+        out_d = torch.empty((n_all, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
+
+        def dense_attend():
+            apbv.approx_attn_prefill(dense, qa, None, None, ka, va, out=out_d)
+
+        dense_attend()
+        torch.cuda.synchronize()
+        dense_ms = median_ms(dense_attend, 3)
+        fl_d = attention_flops([0, n_all], 0, 0, w.hq, w.head_dim)
+        rec["dense_causal"] = {
+            "tokens": n_all, "attention_ms": dense_ms,
+            "tokens_per_s": n_all / (dense_ms * 1e-3),
+            "attention_tflops": fl_d / (dense_ms * 1e-3) / 1e12,
+            "attention_frac_of_peak": fl_d / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        rec["dense_over_approx_layer_time"] = dense_ms / layer_ms
+    torch.cuda.synchronize()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +329,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--other-workloads", default="c1,c3,c4",
+                    help="workloads timed beside the headline one (one layer each; the "
+                         "variable-frame 128K one also times dense causal attention)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -259,15 +340,22 @@ def main():
               "GPU are not part of this build.", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-    import sequence_approximate_attention_score_amd as apbv
     from synthetic import generate, sweep_layouts, workload
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
     w = workload(args.workload)
     print(f"# generating {w.name}: {w.description}", file=sys.stderr, flush=True)
     x = generate(w)
+    # the CPU oracle runs first, in its own worker processes, before the GPU is initialised
+    cpu_rec = None
+    if not (args.profile or args.no_cpu_baseline):
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu_rec, _ = cpu_baseline(x)
+
+    import torch
+    import sequence_approximate_attention_score_amd as apbv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
     up = lambda n: torch.from_numpy(x.bits[n].view(np.int16)).to(dev).view(torch.bfloat16)
     d = {n: up(n) for n in ("q_query", "q_ctx", "k_ctx", "v_ctx", "k_anchor", "v_anchor",
                             "k_query", "v_query")}
@@ -432,11 +520,13 @@ def main():
                                   if layer_two_ms else None),
         "gather_GBps": gather_bytes(lay, w.head_dim) / (float(per[:, 1].mean()) * 1e-3) / 1e9,
         "sweep": sweep or None,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu_rec,
     }
-    if not (args.profile or args.no_cpu_baseline):
-        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"], _ = cpu_baseline(x)
+    if not args.profile and args.other_workloads:
+        del d, ws, sel, kp, vp, out, q_ws, q_out
+        torch.cuda.empty_cache()
+        rec["other_workloads"] = [other_workload(name, dev) for name in
+                                  args.other_workloads.split(",") if name != w.name]
     print(json.dumps(rec), flush=True)
 
 
