@@ -88,7 +88,7 @@ apbv_status apbv_score_select_workspace(const apbv_layout* layout, size_t* bytes
  * (each block's scores sum to G * l_query), computed in fp32 from bf16 inputs with a fixed
  * reduction order (bitwise reproducible). sel[v, g, :] receives the l_pass rows of block v
  * with the largest scores, ties to the lower row, as absolute context rows in ascending order.
- * G * l_query is limited by LDS (about 23000 score rows at head_dim 128; larger gives
+ * G * l_query is limited by LDS (about 32000 score rows at head_dim 128; larger gives
  * APBV_EUNSUPPORTED).
  *
  *   q_query   [l_query, hq, d] bf16, contiguous

@@ -27,12 +27,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKeyTile = 64;        // keys per LDS tile in the row-statistics kernel
 constexpr int kColKeys = 256;       // keys per column-sum workgroup (64 per wave)
-constexpr int kQChunk = 128;        // query rows staged in LDS at a time (column sums)
+constexpr int kQChunk = 64;         // query rows staged in LDS at a time (column sums)
 constexpr float kTau = 8.0f;        // log2 headroom of the lazy row offset (row statistics)
 
 // ------------------------------------------------------------------ 1. row statistics
 template <int D>
-__global__ __launch_bounds__(kThreads) void score_rowstats(const ScoreParams p) {
+__global__ __launch_bounds__(kThreads, 4) void score_rowstats(const ScoreParams p) {
   constexpr int NK = D / 16;
   constexpr int KSTR = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKeyTile * KSTR];
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void score_rowstats(const ScoreParams p) 
 
 // ------------------------------------------------------------------ 2. column sums
 template <int D>
-__global__ __launch_bounds__(kThreads) void score_colsum(const ScoreParams p, int rows_pad) {
+__global__ __launch_bounds__(kThreads, 3) void score_colsum(const ScoreParams p, int rows_pad) {
   constexpr int NK = D / 16;
   constexpr int QSTR = D + 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
