@@ -412,8 +412,16 @@ def main():
     q_ms = median_ms(query_rows, 2 if args.profile else 5)
     bucket_ms, cold_ms = None, None
     if not args.profile:
-        bucket_ms = [median_ms(lambda b=b: attention(b, b + 1), 3)
-                     for b in range(apbv.num_buckets(lay))]
+        # every bucket once untimed, then five round-robin passes (a bucket timed first
+        # right after other work reads as slower than it is)
+        nb = apbv.num_buckets(lay)
+        for b in range(nb):
+            attention(b, b + 1)
+        per_b = [[] for _ in range(nb)]
+        for _ in range(5):
+            for b in range(nb):
+                per_b[b].append(median_ms(lambda b=b: attention(b, b + 1), 1))
+        bucket_ms = [float(np.median(v)) for v in per_b]
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         cold_ms = median_ms(attention, 5, before=lambda: flush.fill_(1))
         del flush
