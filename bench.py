@@ -358,7 +358,7 @@ def main():
     dev = torch.device("cuda:0")
     up = lambda n: torch.from_numpy(x.bits[n].view(np.int16)).to(dev).view(torch.bfloat16)
     d = {n: up(n) for n in ("q_query", "q_ctx", "k_ctx", "v_ctx", "k_anchor", "v_anchor",
-                            "k_query", "v_query")}
+                            "k_query", "v_query", "q_anchor")}
     lay = apbv.Layout(x.block_starts, l_anchor=w.l_anchor, l_query=w.l_query, l_pass=w.l_pass,
                       hq=w.hq, hkv=w.hkv, head_dim=w.head_dim, zigzag=True)
     ws = torch.empty(max(apbv.score_select_workspace(lay), 256), dtype=torch.uint8, device=dev)
@@ -442,6 +442,20 @@ def main():
         layer_two_ms = median_ms(lambda: one_call(aux), 9)
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         plan = apbv.prefill_layer_plan(lay, cus)
+    # every row of the layer in one call (apbv_layer_forward): anchor rows (dense causal over
+    # the anchor), context rows, query rows, on one stream
+    every_row_ms = None
+    if not args.profile:
+        l_ws = torch.empty(max(apbv.layer_workspace(lay), 256), dtype=torch.uint8, device=dev)
+
+        def every_row():
+            apbv.layer_forward(lay, **{n: d[n] for n in (
+                "q_anchor", "k_anchor", "v_anchor", "q_ctx", "k_ctx", "v_ctx", "q_query",
+                "k_query", "v_query")}, workspace=l_ws)
+        every_row()
+        torch.cuda.synchronize()
+        every_row_ms = median_ms(every_row, 5)
+        del l_ws
     # the bucket-count sweep (2, 4, 6, 8 buckets) and the anchor-only baseline (l_p = 0) on
     # the same context, each as one layer: score_select -> gather_passing -> attention
     sweep = []
@@ -524,6 +538,9 @@ def main():
         "layer_one_call_ms": layer_one_ms,
         "layer_two_stream_ms": layer_two_ms,
         "layer_two_stream_tokens_per_s": x.N / (layer_two_ms * 1e-3) if layer_two_ms else None,
+        "layer_every_row_ms": every_row_ms,
+        "layer_every_row_tokens_per_s": ((w.l_anchor + x.N + w.l_query) / (every_row_ms * 1e-3)
+                                         if every_row_ms else None),
         "layer_two_stream_plan": ({"late_bucket_begin": plan[0], "early_blocks": plan[1]}
                                   if layer_two_ms else None),
         "gather_GBps": gather_bytes(lay, w.head_dim) / (float(per[:, 1].mean()) * 1e-3) / 1e9,

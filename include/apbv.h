@@ -243,6 +243,60 @@ apbv_status apbv_query_forward(const apbv_layout* layout, const apbv_bf16* q_que
                                float* lse, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/*
+ * Every row of one layer in one call: the anchor rows, the context rows (steps 1-3) and the
+ * query rows, all on one stream, in that order. The page's sequence is [anchor | context
+ * blocks | query block] (Metodologia, "Suddivisione del Contesto e Disposizione ZigZag");
+ * the anchor opens it, so its rows are dense causal attention over the anchor alone (the
+ * case "Limitazioni" names: one block is plain attention), computed by the same kernel as
+ * the context rows with one block, no prefix. Context rows are bit-identical to
+ * apbv_score_select + apbv_gather_passing + apbv_approx_attn_prefill and query rows to
+ * apbv_query_forward over the same buffers.
+ *
+ * Fields of apbv_layer_io (shapes as in the calls named):
+ *   q_anchor     [l_anchor, hq, d] bf16, contiguous (needed when anchor_out is set)
+ *   k_anchor, v_anchor, k_ctx, v_ctx, k_pre, v_pre, sel:   as apbv_gather_passing
+ *   q_ctx, out, lse:                                       as apbv_approx_attn_prefill
+ *   q_query, scores:                                       as apbv_score_select
+ *   k_query, v_query, query_out, query_lse:   as apbv_query_forward's k/v_query, out, lse
+ *   anchor_out   [l_anchor, hq, d] bf16 out, contiguous; NULL skips the anchor rows
+ *   anchor_lse   [hq, l_anchor] fp32 out, or NULL
+ *   query_out    NULL skips the query rows (then k_query, v_query may be NULL)
+ *   workspace    device buffer of at least apbv_layer_workspace() bytes, 256-byte aligned
+ *                (scoring statistics, scores when `scores` is NULL, query partials; no
+ *                initialisation needed; calls that overlap in time must not share it)
+ * Everything is validated before the first launch; an error launches nothing.
+ */
+typedef struct apbv_layer_io {
+  const apbv_bf16* q_anchor;
+  const apbv_bf16* k_anchor;
+  const apbv_bf16* v_anchor;
+  const apbv_bf16* q_ctx;
+  const apbv_bf16* k_ctx;
+  const apbv_bf16* v_ctx;
+  const apbv_bf16* q_query;
+  const apbv_bf16* k_query;
+  const apbv_bf16* v_query;
+  float* scores;
+  int32_t* sel;
+  apbv_bf16* k_pre;
+  apbv_bf16* v_pre;
+  apbv_bf16* anchor_out;
+  float* anchor_lse;
+  apbv_bf16* out;
+  float* lse;
+  apbv_bf16* query_out;
+  float* query_lse;
+  void* workspace;
+  size_t workspace_bytes;
+} apbv_layer_io;
+
+/* Workspace bytes needed by apbv_layer_forward for this layout (written to *bytes). */
+apbv_status apbv_layer_workspace(const apbv_layout* layout, size_t* bytes);
+
+apbv_status apbv_layer_forward(const apbv_layout* layout, const apbv_layer_io* io,
+                               void* stream);
+
 /* Number of schedulable ranges: ZigZag buckets (ceil(n/2)) if zigzag, else n_blocks.
  * Returns -1 for an invalid layout. Host only. */
 int32_t apbv_num_buckets(const apbv_layout* layout);

@@ -22,7 +22,7 @@ EXPORTED = ["apbv_score_select_workspace", "apbv_score_select", "apbv_gather_pas
             "apbv_approx_attn_prefill", "apbv_query_forward_workspace", "apbv_query_forward",
             "apbv_num_buckets", "apbv_schedule", "apbv_attn_tile_rows", "apbv_status_str",
             "apbv_last_error", "apbv_version", "apbv_prefill_layer", "apbv_prefill_layer_plan",
-            "apbv_score_select_noalloc"]
+            "apbv_score_select_noalloc", "apbv_layer_workspace", "apbv_layer_forward"]
 
 
 class ApbvError(RuntimeError):
@@ -41,6 +41,14 @@ class _Layout(ctypes.Structure):
 
 _VP, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _LP = ctypes.POINTER(_Layout)
+
+_IO_FIELDS = ["q_anchor", "k_anchor", "v_anchor", "q_ctx", "k_ctx", "v_ctx", "q_query",
+              "k_query", "v_query", "scores", "sel", "k_pre", "v_pre", "anchor_out",
+              "anchor_lse", "out", "lse", "query_out", "query_lse", "workspace"]
+
+
+class _LayerIO(ctypes.Structure):
+    _fields_ = [(f, _VP) for f in _IO_FIELDS] + [("workspace_bytes", _SZ)]
 _lib = None
 
 
@@ -61,6 +69,8 @@ def lib() -> ctypes.CDLL:
             "apbv_query_forward": (_I32, [_LP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           _SZ, _VP]),
             "apbv_prefill_layer": (_I32, [_LP] + [_VP] * 13 + [_SZ] + [_VP] * 4 + [_I32]),
+            "apbv_layer_workspace": (_I32, [_LP, ctypes.POINTER(_SZ)]),
+            "apbv_layer_forward": (_I32, [_LP, ctypes.POINTER(_LayerIO), _VP]),
             "apbv_prefill_layer_plan": (_I32, [_LP, _I32, ctypes.POINTER(_I32),
                                                ctypes.POINTER(_I32)]),
             "apbv_num_buckets": (_I32, [_LP]),
@@ -405,6 +415,71 @@ def prefill_layer(layout: Layout, q_query, q_ctx, k_ctx, v_ctx, k_anchor, v_anch
                                     _stream(dev), aux, ready, done, int(compute_units)),
            "apbv_prefill_layer")
     return out, lse, sel, scores
+
+
+def layer_workspace(layout: Layout) -> int:
+    n = _SZ(0)
+    _check(lib().apbv_layer_workspace(layout.ref(), ctypes.byref(n)), "apbv_layer_workspace")
+    return n.value
+
+
+def layer_forward(layout: Layout, *, q_anchor, k_anchor, v_anchor, q_ctx, k_ctx, v_ctx,
+                  q_query, k_query, v_query, anchor_rows: bool = True, query_rows: bool = True,
+                  want_lse: bool = False, want_scores: bool = False, workspace=None):
+    """Every row of one layer in one call on the current stream: anchor rows (dense causal
+    over the anchor), context rows (score/select, gather, approximate attention) and query
+    rows (exact over the whole sequence). Returns a dict with ``anchor_out``, ``out``,
+    ``query_out`` (None when skipped), their lse (``anchor_lse``, ``lse``, ``query_lse``;
+    None unless ``want_lse``), ``sel``, ``k_pre``, ``v_pre`` and ``scores``."""
+    import torch
+    dev = k_ctx.device
+    L, d, bf, f32 = layout, layout.head_dim, torch.bfloat16, torch.float32
+    do_anchor = anchor_rows and L.l_anchor > 0
+    do_query = query_rows and L.l_query > 0
+
+    def new(shape, dtype, cond=True):
+        return torch.empty(shape, dtype=dtype, device=dev) if cond else None
+
+    r = dict(
+        anchor_out=new((L.l_anchor, L.hq, d), bf, do_anchor),
+        anchor_lse=new((L.hq, L.l_anchor), f32, do_anchor and want_lse),
+        out=new((L.n_tokens, L.hq, d), bf),
+        lse=new((L.hq, L.n_tokens), f32, want_lse),
+        query_out=new((L.l_query, L.hq, d), bf, do_query),
+        query_lse=new((L.hq, L.l_query), f32, do_query and want_lse),
+        sel=new((L.n_blocks, L.hkv, L.l_pass), torch.int32),
+        k_pre=new((L.hkv, L.pre_rows, d), bf),
+        v_pre=new((L.hkv, L.pre_rows, d), bf),
+        scores=new((L.hkv, L.n_tokens), f32, want_scores))
+    if workspace is None:
+        workspace = torch.empty(max(layer_workspace(layout), 256), dtype=torch.uint8,
+                                device=dev)
+    has_anchor, has_pre = L.l_anchor > 0, L.pre_rows > 0
+    checked = [
+        _arg(q_anchor, "q_anchor", bf, L.l_anchor, L.hq * d, required=do_anchor),
+        _arg(k_anchor, "k_anchor", bf, L.l_anchor, L.hkv * d, required=has_anchor),
+        _arg(v_anchor, "v_anchor", bf, L.l_anchor, L.hkv * d, required=has_anchor),
+        _arg(q_ctx, "q_ctx", bf, L.n_tokens, L.hq * d, L.q_stride),
+        _arg(k_ctx, "k_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(v_ctx, "v_ctx", bf, L.n_tokens, L.hkv * d, L.kv_stride),
+        _arg(q_query, "q_query", bf, L.l_query, L.hq * d, required=L.l_query > 0),
+        _arg(k_query, "k_query", bf, L.l_query, L.hkv * d, required=do_query),
+        _arg(v_query, "v_query", bf, L.l_query, L.hkv * d, required=do_query),
+        _arg(r["scores"], "scores", f32, L.hkv, L.n_tokens, required=False),
+        _arg(r["sel"], "sel", torch.int32, L.n_blocks, L.hkv * L.l_pass),
+        _arg(r["k_pre"], "k_pre", bf, L.hkv, L.pre_rows * d, required=has_pre),
+        _arg(r["v_pre"], "v_pre", bf, L.hkv, L.pre_rows * d, required=has_pre),
+        _arg(r["anchor_out"], "anchor_out", bf, L.l_anchor, L.hq * d, required=False),
+        _arg(r["anchor_lse"], "anchor_lse", f32, L.hq, L.l_anchor, required=False),
+        _arg(r["out"], "out", bf, L.n_tokens, L.hq * d),
+        _arg(r["lse"], "lse", f32, L.hq, L.n_tokens, required=False),
+        _arg(r["query_out"], "query_out", bf, L.l_query, L.hq * d, required=False),
+        _arg(r["query_lse"], "query_lse", f32, L.hq, L.l_query, required=False),
+        _arg(workspace, "workspace", torch.uint8, workspace.numel(), 1)]
+    io = _LayerIO(*_pointers(*checked), workspace.numel())
+    _check(lib().apbv_layer_forward(L.ref(), ctypes.byref(io), _stream(dev)),
+           "apbv_layer_forward")
+    return r
 
 
 def version() -> str:

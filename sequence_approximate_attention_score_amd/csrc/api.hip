@@ -284,6 +284,97 @@ apbv_status launch_attn_range(AttnParams& p, const Checked& c, int range_begin, 
   return APBV_OK;
 }
 
+// Split of the whole-layer workspace: the scoring part (statistics and scores), rounded up
+// to 256 bytes; the query partials follow it.
+size_t layer_workspace_split(const Checked& c) {
+  const size_t w = score_workspace_bytes(c.n, c.hkv, c.G * c.l_q, n_split_of(c), c.N, true);
+  return (w + 255) & ~(size_t)255;
+}
+
+// Checks of the query-row call and its parameters.
+apbv_status query_params(const Checked& c, const apbv_bf16* q_query, const apbv_bf16* k_query,
+                         const apbv_bf16* v_query, const apbv_bf16* k_anchor,
+                         const apbv_bf16* v_anchor, const apbv_bf16* k_ctx,
+                         const apbv_bf16* v_ctx, apbv_bf16* out, float* lse, void* workspace,
+                         size_t workspace_bytes, QueryParams& p, QueryPlan& q) {
+  const bool any = c.l_q > 0;
+  APBV_TRY(check_ptr(q_query, "q_query", any));
+  APBV_TRY(check_ptr(k_query, "k_query", any));
+  APBV_TRY(check_ptr(v_query, "v_query", any));
+  APBV_TRY(check_ptr(k_anchor, "k_anchor", any && c.l_a > 0));
+  APBV_TRY(check_ptr(v_anchor, "v_anchor", any && c.l_a > 0));
+  APBV_TRY(check_ptr(k_ctx, "k_ctx", any));
+  APBV_TRY(check_ptr(v_ctx, "v_ctx", any));
+  APBV_TRY(check_ptr(out, "out", any));
+  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return fail(APBV_EINVAL, "lse is not 4-byte aligned");
+  q = plan_query(c.l_a, c.N, c.l_q, c.hq, c.hkv, c.d);
+  const size_t need = any ? q.o_bytes + q.lse_bytes : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(APBV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (workspace != nullptr && ((uintptr_t)workspace & 255u) != 0)
+    return fail(APBV_EINVAL, "workspace is not 256-byte aligned");
+  if ((uint64_t)q.row_tiles * c.hkv * q.n_chunks >= (1ull << 31))
+    return fail(APBV_EUNSUPPORTED, "query grid too large");
+  memset(&p, 0, sizeof(p));
+  p.qq = q_query;
+  p.kq = k_query;
+  p.vq = v_query;
+  p.ka = k_anchor;
+  p.va = v_anchor;
+  p.kc = k_ctx;
+  p.vc = v_ctx;
+  p.part_o = reinterpret_cast<float*>(workspace);
+  p.part_lse = workspace == nullptr
+                   ? nullptr
+                   : reinterpret_cast<float*>(static_cast<char*>(workspace) + q.o_bytes);
+  p.out = out;
+  p.lse = lse;
+  p.kv_stride = c.kv_stride;
+  p.hq = c.hq;
+  p.hkv = c.hkv;
+  p.group = c.G;
+  p.l_query = c.l_q;
+  p.l_anchor = c.l_a;
+  p.n_tokens = c.N;
+  p.chunk_keys = q.chunk_keys;
+  p.n_anchor_chunks = q.n_anchor_chunks;
+  p.n_ctx_chunks = q.n_ctx_chunks;
+  p.n_query_chunks = q.n_query_chunks;
+  p.n_chunks = q.n_chunks;
+  p.row_tiles = q.row_tiles;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+  return APBV_OK;
+}
+
+// Attention parameters of the anchor rows: the anchor opens the sequence, so its rows are
+// dense causal attention over the anchor alone (one block, no prefix).
+apbv_status anchor_params(const Checked& c, const apbv_bf16* q_anchor, const apbv_bf16* k_anchor,
+                          const apbv_bf16* v_anchor, apbv_bf16* out, float* lse, AttnParams& p) {
+  APBV_TRY(check_ptr(q_anchor, "q_anchor", true));
+  APBV_TRY(check_ptr(k_anchor, "k_anchor", true));
+  APBV_TRY(check_ptr(v_anchor, "v_anchor", true));
+  APBV_TRY(check_ptr(out, "anchor_out", true));
+  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0)
+    return fail(APBV_EINVAL, "anchor_lse is not 4-byte aligned");
+  memset(&p, 0, sizeof(p));
+  const int32_t bs[2] = {0, c.l_a};
+  build_schedule(p.sched, 1, bs, 1, attn_tile_rows(c.d));
+  p.q = q_anchor;
+  p.kc = k_anchor;
+  p.vc = v_anchor;
+  p.out = out;
+  p.lse = lse;
+  p.q_stride = (int64_t)c.hq * c.d;
+  p.kv_stride = (int64_t)c.hkv * c.d;
+  p.hq = c.hq;
+  p.hkv = c.hkv;
+  p.group = c.G;
+  p.n_tokens = c.l_a;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+  return APBV_OK;
+}
+
 // Split of one layer for the two-stream overlap. Attention of the buckets [late, n_buckets)
 // needs the selections of blocks [0, early) only: with ZigZag, bucket b holds blocks b and
 // n-1-b, so the late set's highest block is n-1-late and early = n-1-late. The late set is
@@ -544,59 +635,74 @@ apbv_status apbv_query_forward(const apbv_layout* layout, const apbv_bf16* q_que
                                void* stream) {
   Checked c;
   APBV_TRY(check_layout(layout, c));
-  const bool any = c.l_q > 0;
-  APBV_TRY(check_ptr(q_query, "q_query", any));
-  APBV_TRY(check_ptr(k_query, "k_query", any));
-  APBV_TRY(check_ptr(v_query, "v_query", any));
-  APBV_TRY(check_ptr(k_anchor, "k_anchor", any && c.l_a > 0));
-  APBV_TRY(check_ptr(v_anchor, "v_anchor", any && c.l_a > 0));
-  APBV_TRY(check_ptr(k_ctx, "k_ctx", any));
-  APBV_TRY(check_ptr(v_ctx, "v_ctx", any));
-  APBV_TRY(check_ptr(out, "out", any));
-  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return fail(APBV_EINVAL, "lse is not 4-byte aligned");
-  const QueryPlan q = plan_query(c.l_a, c.N, c.l_q, c.hq, c.hkv, c.d);
-  const size_t need = any ? q.o_bytes + q.lse_bytes : 0;
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(APBV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  if (workspace != nullptr && ((uintptr_t)workspace & 255u) != 0)
-    return fail(APBV_EINVAL, "workspace is not 256-byte aligned");
-  if ((uint64_t)q.row_tiles * c.hkv * q.n_chunks >= (1ull << 31))
-    return fail(APBV_EUNSUPPORTED, "query grid too large");
-  if (!any) {
-    g_err[0] = 0;
-    return APBV_OK;
-  }
-
   QueryParams p;
-  memset(&p, 0, sizeof(p));
-  p.qq = q_query;
-  p.kq = k_query;
-  p.vq = v_query;
-  p.ka = k_anchor;
-  p.va = v_anchor;
-  p.kc = k_ctx;
-  p.vc = v_ctx;
-  p.part_o = reinterpret_cast<float*>(workspace);
-  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + q.o_bytes);
-  p.out = out;
-  p.lse = lse;
-  p.kv_stride = c.kv_stride;
-  p.hq = c.hq;
-  p.hkv = c.hkv;
-  p.group = c.G;
-  p.l_query = c.l_q;
-  p.l_anchor = c.l_a;
-  p.n_tokens = c.N;
-  p.chunk_keys = q.chunk_keys;
-  p.n_anchor_chunks = q.n_anchor_chunks;
-  p.n_ctx_chunks = q.n_ctx_chunks;
-  p.n_query_chunks = q.n_query_chunks;
-  p.n_chunks = q.n_chunks;
-  p.row_tiles = q.row_tiles;
-  p.scale_log2 = c.scale * 1.4426950408889634f;
-  const hipError_t e = launch_query(p, c.d, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(APBV_EHIP, "query forward launch: %s", hipGetErrorString(e));
+  QueryPlan q;
+  APBV_TRY(query_params(c, q_query, k_query, v_query, k_anchor, v_anchor, k_ctx, v_ctx, out, lse,
+                        workspace, workspace_bytes, p, q));
+  if (c.l_q > 0) {
+    const hipError_t e = launch_query(p, c.d, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(APBV_EHIP, "query forward launch: %s", hipGetErrorString(e));
+  }
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_layer_workspace(const apbv_layout* layout, size_t* bytes) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  if (bytes == nullptr) return fail(APBV_EINVAL, "bytes is NULL");
+  *bytes = layer_workspace_split(c);
+  const QueryPlan q = plan_query(c.l_a, c.N, c.l_q, c.hq, c.hkv, c.d);
+  *bytes += c.l_q > 0 ? q.o_bytes + q.lse_bytes : 0;
+  g_err[0] = 0;
+  return APBV_OK;
+}
+
+apbv_status apbv_layer_forward(const apbv_layout* layout, const apbv_layer_io* io,
+                               void* stream) {
+  Checked c;
+  APBV_TRY(check_layout(layout, c));
+  if (io == nullptr) return fail(APBV_EINVAL, "io is NULL");
+  hipStream_t s0 = (hipStream_t)stream;
+  const size_t split = layer_workspace_split(c);
+  if (io->workspace != nullptr && ((uintptr_t)io->workspace & 255u) != 0)
+    return fail(APBV_EINVAL, "workspace is not 256-byte aligned");
+  if (io->workspace_bytes < split && split > 0)
+    return fail(APBV_EWORKSPACE, "workspace of at least %zu bytes needed, %zu given", split,
+                io->workspace_bytes);
+  // every part is validated before anything is launched
+  const bool anchor_rows = io->anchor_out != nullptr && c.l_a > 0;
+  AttnParams anc;
+  if (anchor_rows) {
+    APBV_TRY(anchor_params(c, io->q_anchor, io->k_anchor, io->v_anchor, io->anchor_out,
+                           io->anchor_lse, anc));
+  }
+  ScoreParams sp;
+  APBV_TRY(score_params(layout, c, io->q_query, io->k_ctx, io->scores, io->sel, io->workspace,
+                        split, sp));
+  GatherParams gp;
+  APBV_TRY(gather_params(layout, c, io->k_anchor, io->v_anchor, io->k_ctx, io->v_ctx, io->sel,
+                         io->k_pre, io->v_pre, nullptr, gp));
+  AttnParams ap;
+  APBV_TRY(attn_params(layout, c, io->q_ctx, io->k_pre, io->v_pre, io->k_ctx, io->v_ctx,
+                       io->out, io->lse, ap));
+  const bool query_rows = io->query_out != nullptr && c.l_q > 0;
+  QueryParams qp;
+  QueryPlan qplan;
+  if (query_rows) {
+    char* qws = io->workspace == nullptr ? nullptr : static_cast<char*>(io->workspace) + split;
+    APBV_TRY(query_params(c, io->q_query, io->k_query, io->v_query, io->k_anchor, io->v_anchor,
+                          io->k_ctx, io->v_ctx, io->query_out, io->query_lse, qws,
+                          io->workspace_bytes - split, qp, qplan));
+  }
+  hipError_t e;
+  if (anchor_rows) APBV_TRY(launch_attn_range(anc, c, 0, 1, s0));
+  if ((e = launch_score_select(sp, c.d, c.max_block, s0)) != hipSuccess ||
+      (e = launch_gather(gp, c.d, s0)) != hipSuccess)
+    return fail(APBV_EHIP, "layer launch: %s", hipGetErrorString(e));
+  APBV_TRY(launch_attn_range(ap, c, 0, ap.sched.n_buckets(), s0));
+  if (query_rows && (e = launch_query(qp, c.d, s0)) != hipSuccess)
+    return fail(APBV_EHIP, "query forward launch: %s", hipGetErrorString(e));
   g_err[0] = 0;
   return APBV_OK;
 }

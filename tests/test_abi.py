@@ -372,3 +372,43 @@ def test_noalloc_scoring_rejects_layouts_beyond_its_scratch_before_launch():
     ws = ctypes.c_size_t(0)
     assert L.apbv_score_select_workspace(big.ref(), ctypes.byref(ws)) == 0
     assert ws.value > 16 << 20
+
+
+def test_layer_forward_validation_before_launch():
+    """The whole-layer call checks every part (anchor, context, query rows and the shared
+    workspace) before the first launch; each call below fails on the host."""
+    lay = small_layout()                              # N=900, l_a=64, l_q=32, hq=4, d=128
+    L = apbv.lib()
+    n_layer, n_score, n_query = (ctypes.c_size_t(0) for _ in range(3))
+    assert L.apbv_layer_workspace(lay.ref(), ctypes.byref(n_layer)) == 0
+    assert L.apbv_score_select_workspace(lay.ref(), ctypes.byref(n_score)) == 0
+    assert L.apbv_query_forward_workspace(lay.ref(), ctypes.byref(n_query)) == 0
+    split = -(-n_score.value // 256) * 256
+    assert n_layer.value == split + n_query.value
+    base = {f: 0x1000 * (i + 1) for i, f in enumerate(_lib._IO_FIELDS)}
+    base["workspace"] = 0x100000
+
+    def call(ws_bytes=None, **over):
+        p = dict(base, **over)
+        io = _lib._LayerIO(*(p[f] for f in _lib._IO_FIELDS),
+                           n_layer.value if ws_bytes is None else ws_bytes)
+        return L.apbv_layer_forward(lay.ref(), ctypes.byref(io), None)
+
+    assert L.apbv_layer_forward(lay.ref(), None, None) == _lib.APBV_EINVAL
+    assert call(q_anchor=None) == _lib.APBV_EINVAL            # anchor rows asked for
+    assert call(anchor_out=0x7008) == _lib.APBV_EINVAL        # misaligned
+    assert call(anchor_lse=0x7002) == _lib.APBV_EINVAL
+    assert call(k_query=None) == _lib.APBV_EINVAL             # query rows asked for
+    assert call(query_lse=0x9002) == _lib.APBV_EINVAL
+    assert call(q_ctx=None) == _lib.APBV_EINVAL
+    assert call(workspace=0x100010) == _lib.APBV_EINVAL       # not 256-byte aligned
+    assert call(workspace=None) == _lib.APBV_EWORKSPACE
+    assert call(ws_bytes=split - 1) == _lib.APBV_EWORKSPACE   # scoring part short
+    # the query partials follow the scoring part
+    assert call(ws_bytes=n_layer.value - 1) == _lib.APBV_EWORKSPACE
+    # without query rows the scoring part is enough; then a bad context pointer still fails
+    assert call(ws_bytes=split, query_out=None, k_query=None, v_query=None,
+                out=0x6008) == _lib.APBV_EINVAL
+    bad = small_layout(head_dim=96)
+    io = _lib._LayerIO(*(base[f] for f in _lib._IO_FIELDS), 1 << 20)
+    assert L.apbv_layer_forward(bad.ref(), ctypes.byref(io), None) == _lib.APBV_EUNSUPPORTED
