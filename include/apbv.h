@@ -95,7 +95,10 @@ apbv_status apbv_score_select_workspace(const apbv_layout* layout, size_t* bytes
  *   k_ctx     [N, hkv, d] bf16 (kv_row_stride)
  *   scores    [hkv, N] fp32 out, or NULL (then kept in the workspace)
  *   sel       [n_blocks, hkv, l_pass] int32 out
- *   workspace device buffer of at least apbv_score_select_workspace() bytes
+ *   workspace device buffer of at least apbv_score_select_workspace() bytes, 256-byte
+ *             aligned: split row statistics, the score rows packed per KV head, and the
+ *             scores when `scores` is NULL (no initialisation needed; calls that overlap in
+ *             time must not share it)
  */
 apbv_status apbv_score_select(const apbv_layout* layout, const apbv_bf16* q_query,
                               const apbv_bf16* k_ctx, float* scores, int32_t* sel,

@@ -115,11 +115,13 @@ hipError_t launch_query(const QueryParams& p, int head_dim, hipStream_t stream);
 struct ScoreParams {
   const uint16_t* qq;   // [l_q, hq, d]
   const uint16_t* kc;   // [N, hkv, d] with kv_stride
+  uint16_t* qp;         // [hkv, q_rows, d] packed score rows (workspace)
   float* scores;        // [hkv, N]
   float2* stats;        // [n_blocks, hkv, n_split, rows] (max in log2 units, sum)
   int32_t* sel;         // [n_blocks, hkv, l_pass]
   int64_t kv_stride;
   int32_t hq, hkv, group, l_query, rows;   // rows = group * l_query
+  int32_t q_rows;                          // rows rounded up to a multiple of 128
   int32_t n_tokens, n_blocks, n_split, l_pass;
   int32_t v_begin, v_count;   // blocks scored and selected by one launch
   float scale_log2;
@@ -128,8 +130,18 @@ struct ScoreParams {
 
 constexpr int kScoreSplit = 2048;   // keys per row-statistics workgroup
 
-size_t score_workspace_bytes(int n_blocks, int hkv, int rows, int n_split, int n_tokens,
-                             bool need_scores);
+// Scoring workspace: split statistics, packed score rows, then (when the caller passes no
+// score buffer) the scores, each part 256-byte aligned.
+struct ScoreWorkspace {
+  size_t stats, qpack, scores, total;   // byte offsets of the parts, and the size
+};
+ScoreWorkspace score_workspace(int n_blocks, int hkv, int rows, int n_split, int n_tokens,
+                               int head_dim, bool need_scores);
+inline size_t score_workspace_bytes(int n_blocks, int hkv, int rows, int n_split,
+                                    int n_tokens, int head_dim, bool need_scores) {
+  return score_workspace(n_blocks, hkv, rows, n_split, n_tokens, head_dim, need_scores).total;
+}
+inline int score_q_rows(int rows) { return (rows + 127) / 128 * 128; }
 // LDS of one column-sum workgroup (two staged query chunks and the rows' log-sum-exps)
 size_t score_colsum_lds_bytes(int rows, int head_dim);
 constexpr size_t kMaxLdsBytes = 160 * 1024;   // per workgroup on gfx950

@@ -169,7 +169,8 @@ apbv_status score_params(const apbv_layout* layout, const Checked& c, const apbv
   if (score_colsum_lds_bytes(rows, c.d) > kMaxLdsBytes)
     return fail(APBV_EUNSUPPORTED, "G * l_query = %d score rows exceed the column-sum LDS", rows);
   const int n_split = n_split_of(c);
-  const size_t need = score_workspace_bytes(c.n, c.hkv, rows, n_split, c.N, scores == nullptr);
+  const ScoreWorkspace ws = score_workspace(c.n, c.hkv, rows, n_split, c.N, c.d, scores == nullptr);
+  const size_t need = ws.total;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(APBV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
@@ -179,10 +180,10 @@ apbv_status score_params(const apbv_layout* layout, const Checked& c, const apbv
   memset(&p, 0, sizeof(p));
   p.qq = q_query;
   p.kc = k_ctx;
-  p.stats = reinterpret_cast<float2*>(workspace);
-  const size_t stats_bytes = (((size_t)c.n * c.hkv * n_split * rows * sizeof(float2)) + 255) & ~(size_t)255;
-  p.scores = scores != nullptr ? scores
-                               : reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes);
+  char* w = static_cast<char*>(workspace);
+  p.stats = reinterpret_cast<float2*>(w + ws.stats);
+  p.qp = reinterpret_cast<uint16_t*>(w + ws.qpack);
+  p.scores = scores != nullptr ? scores : reinterpret_cast<float*>(w + ws.scores);
   p.sel = sel;
   p.kv_stride = c.kv_stride;
   p.hq = c.hq;
@@ -190,6 +191,7 @@ apbv_status score_params(const apbv_layout* layout, const Checked& c, const apbv
   p.group = c.G;
   p.l_query = c.l_q;
   p.rows = rows;
+  p.q_rows = score_q_rows(rows);
   p.n_tokens = c.N;
   p.n_blocks = c.n;
   p.n_split = n_split;
@@ -287,7 +289,7 @@ apbv_status launch_attn_range(AttnParams& p, const Checked& c, int range_begin, 
 // Split of the whole-layer workspace: the scoring part (statistics and scores), rounded up
 // to 256 bytes; the query partials follow it.
 size_t layer_workspace_split(const Checked& c) {
-  const size_t w = score_workspace_bytes(c.n, c.hkv, c.G * c.l_q, n_split_of(c), c.N, true);
+  const size_t w = score_workspace_bytes(c.n, c.hkv, c.G * c.l_q, n_split_of(c), c.N, c.d, true);
   return (w + 255) & ~(size_t)255;
 }
 
@@ -432,7 +434,7 @@ apbv_status apbv_score_select_workspace(const apbv_layout* layout, size_t* bytes
   Checked c;
   APBV_TRY(check_layout(layout, c));
   if (bytes == nullptr) return fail(APBV_EINVAL, "bytes is NULL");
-  *bytes = score_workspace_bytes(c.n, c.hkv, c.G * c.l_q, n_split_of(c), c.N, true);
+  *bytes = score_workspace_bytes(c.n, c.hkv, c.G * c.l_q, n_split_of(c), c.N, c.d, true);
   g_err[0] = 0;
   return APBV_OK;
 }
@@ -456,7 +458,7 @@ apbv_status apbv_score_select_noalloc(const apbv_layout* layout, const apbv_bf16
   Checked c;
   APBV_TRY(check_layout(layout, c));
   const size_t need =
-      score_workspace_bytes(c.n, c.hkv, c.G * c.l_q, n_split_of(c), c.N, scores == nullptr);
+      score_workspace_bytes(c.n, c.hkv, c.G * c.l_q, n_split_of(c), c.N, c.d, scores == nullptr);
   if (need > kScratchBytes)
     return fail(APBV_EUNSUPPORTED,
                 "this layout needs %zu bytes of scratch, the allocation-free entry point has "

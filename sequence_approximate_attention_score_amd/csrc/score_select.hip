@@ -6,7 +6,10 @@
 // Score of key j of block v, KV head g (R = G * l_query score rows, row r = head g*G + r/l_q,
 // query row r % l_q):
 //     s[g, j] = sum_r softmax_{j' in block v}(scale * q_r . k_j')_j
-// Three kernels, all with a fixed reduction order (results are bitwise reproducible):
+// Four kernels, all with a fixed reduction order (results are bitwise reproducible):
+//   0. packing: the score rows of every KV head are laid out contiguously in the workspace,
+//      [hkv][q_rows][d] with zero rows up to a multiple of 128, so both passes below fill
+//      their LDS tiles with buffer loads straight into LDS at fixed per-lane offsets;
 //   1. row statistics: per (block, KV head, 128-row group, 2048-key split) a running offset
 //      (at most kTau below the row max, log2 units) and the sum of exp2 relative to it;
 //      S^T = K . Q^T on MFMA puts one row per lane.
@@ -30,12 +33,79 @@ constexpr int kColKeys = 256;       // keys per column-sum workgroup (64 per wav
 constexpr int kQChunk = 64;         // query rows staged in LDS at a time (column sums)
 constexpr float kTau = 8.0f;        // log2 headroom of the lazy row offset (row statistics)
 
+// A 64-row tile of d-element bf16 rows in LDS, rows padded to d + 8 elements (16 B) so that
+// the MFMA operand reads are free of bank conflicts. It is filled in 1 KB segments (64
+// lanes x 16 B, written in lane order): segment s by wave s % 4 of the workgroup; the
+// padding slot of a row repeats the row's first 16 bytes.
+template <int D>
+struct Tile {
+  static constexpr int STR = D + 8;            // elements per LDS row
+  static constexpr int SLOT = STR / 8;         // 16-byte slots per LDS row
+  static constexpr int SEGS = SLOT;            // 64 rows x SLOT slots / 64 lanes
+  static constexpr int ELEMS = SEGS * 512;     // = 64 * STR
+  static constexpr int LOADS = (SEGS + 3) / 4; // segments per wave
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Byte offsets of this lane's load slots inside a tile whose rows are row_bytes apart
+// (row_bytes < 2^24: a K/V row stride is below 2^23 bytes, a packed row is 2d bytes).
+template <int D>
+struct TileLoader {
+  int off[Tile<D>::LOADS];
+  int wave;   // uniform
+  __device__ __forceinline__ void init(unsigned row_bytes) {
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < Tile<D>::LOADS; ++j) {
+      const int q = (j * 4 + wave) * 64 + lane;
+      const int r = q / Tile<D>::SLOT, c = q % Tile<D>::SLOT;
+      off[j] = (int)__umul24((unsigned)r, row_bytes) + (c < D / 8 ? c * 16 : 0);
+    }
+  }
+  // The tile's rows start at `base`; bytes at or past `bytes` from it read as zero (the
+  // buffer's record count), so rows past the end of the data are never fetched.
+  __device__ __forceinline__ void load(uint16_t* dst, const uint16_t* base, unsigned bytes) const {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, (int)bytes, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < Tile<D>::LOADS; ++j) {
+      const int seg = j * 4 + wave;
+      const int o = off[j];   // (a member passed straight to the builtin loses the host stub)
+      if (seg < Tile<D>::SEGS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + seg * 512), 16, o, 0, 0,
+                                                 0);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ 0. packed score rows
+// Packed row r of KV head g is query row r % l_q of head g*G + r / l_q; rows r >= G*l_q of
+// the padding are zero. One thread per 16 bytes.
+template <int D>
+__global__ __launch_bounds__(kThreads) void score_pack_q(const ScoreParams p) {
+  constexpr int CPR = D / 8;
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= (int64_t)p.hkv * p.q_rows * CPR) return;
+  const int c = (int)(t % CPR);
+  const int64_t gr = t / CPR;
+  const int r = (int)(gr % p.q_rows), g = (int)(gr / p.q_rows);
+  u32x4 val = {0, 0, 0, 0};
+  if (r < p.rows) {
+    const int h = g * p.group + r / p.l_query, qi = r % p.l_query;
+    val = load16(p.qq + ((int64_t)qi * p.hq + h) * D + c * 8);
+  }
+  store16(p.qp + gr * D + c * 8, val);
+}
+
 // ------------------------------------------------------------------ 1. row statistics
 template <int D>
 __global__ __launch_bounds__(kThreads, 4) void score_rowstats(const ScoreParams p) {
+  using T = Tile<D>;
   constexpr int NK = D / 16;
-  constexpr int KSTR = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKeyTile * KSTR];
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t K1[T::ELEMS];
 
   const int n_rg = (p.rows + 127) / 128;
   int b = blockIdx.x;
@@ -50,56 +120,37 @@ __global__ __launch_bounds__(kThreads, 4) void score_rowstats(const ScoreParams 
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int row = rg * 128 + wave * 32 + l32;
+  const int row = rg * 128 + wave * 32 + l32;   // below q_rows (a multiple of 128)
   bf16x8 qf[NK];
   {
-    const bool ok = row < p.rows;
-    const int h = g * p.group + (ok ? row / p.l_query : 0);
-    const int qi = ok ? row % p.l_query : 0;
-    const uint16_t* qrow = p.qq + ((int64_t)qi * p.hq + h) * D + half * 8;
+    const uint16_t* qrow = p.qp + ((int64_t)g * p.q_rows + row) * D + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks)
-      qf[ks] = as_bf16x8(ok ? load16(qrow + ks * 16) : u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < NK; ++ks) qf[ks] = as_bf16x8(load16(qrow + ks * 16));
   }
 
-  // K tiles: the next tile's rows are fetched into registers while the current one is
-  // computed, then stored into the other LDS stage (one barrier per tile)
-  constexpr int CPT = kKeyTile * D / 8 / kThreads;   // 16-byte chunks per thread per tile
-  u32x4 pre[CPT];
-  auto fetch = [&](int k0) {
-    const int valid = min(kKeyTile, k_end - k0);
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = threadIdx.x + c * kThreads;
-      const int kr = idx / (D / 8), col = idx % (D / 8);
-      pre[c] = kr < valid ? load16(p.kc + (int64_t)(k0 + kr) * p.kv_stride + g * D + col * 8)
-                          : u32x4{0, 0, 0, 0};
-    }
+  const unsigned stride_b = (unsigned)p.kv_stride * 2u;
+  TileLoader<D> ld;
+  ld.init(stride_b);
+  auto load = [&](uint16_t* dst, int k0) {
+    ld.load(dst, p.kc + (int64_t)k0 * p.kv_stride + g * D,
+            (unsigned)min(kKeyTile, k_end - k0) * stride_b);
   };
-  fetch(k_begin);
-  int buf = 0;
+  int kofs = l32 * T::STR + half * 8;
+  // an opaque lane offset keeps every LDS read "array + offset", so the reads of one
+  // buffer carry that array's alias information past the loads into the other
+  asm volatile("" : "+v"(kofs));
+
   float m = -INFINITY, l = 0.f;   // raw-logit offset, sum of exp2((s - m) * c) over this lane's keys
-  for (int k0 = k_begin; k0 < k_end; k0 += kKeyTile, buf ^= 1) {
+  auto tile = [&](const uint16_t* kb, int k0) {
     const int valid = min(kKeyTile, k_end - k0);
-    uint16_t* sKb = sK + buf * kKeyTile * KSTR;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = threadIdx.x + c * kThreads;
-      store16(sKb + (idx / (D / 8)) * KSTR + (idx % (D / 8)) * 8, pre[c]);
-    }
-    __syncthreads();
-    if (k0 + kKeyTile < k_end) fetch(k0 + kKeyTile);
     f32x16 s[kKeyTile / 32];
-#pragma unroll
-    for (int n = 0; n < kKeyTile / 32; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[n][r] = 0.f;
+    const f32x16 zero = {};
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
       for (int n = 0; n < kKeyTile / 32; ++n) {
-        const bf16x8 a = as_bf16x8(load16(sKb + (n * 32 + l32) * KSTR + ks * 16 + half * 8));
-        s[n] = mfma32(a, qf[ks], s[n]);
+        const bf16x8 a = as_bf16x8(load16(kb + kofs + n * 32 * T::STR + ks * 16));
+        s[n] = mfma32(a, qf[ks], ks == 0 ? zero : s[n]);
       }
     if (valid < kKeyTile) {   // ragged last tile: keys past the split end drop out
 #pragma unroll
@@ -127,6 +178,22 @@ __global__ __launch_bounds__(kThreads, 4) void score_rowstats(const ScoreParams 
     for (int n = 0; n < kKeyTile / 32; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) l += fast_exp2(fmaf(s[n][r], p.scale_log2, -mc));
+  };
+
+  // two LDS stages: tile i+1 is loaded while tile i is computed, one barrier per tile
+  load(K0, k_begin);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int k0 = k_begin; k0 < k_end; k0 += 2 * kKeyTile) {
+    if (k0 + kKeyTile < k_end) load(K1, k0 + kKeyTile);
+    tile(K0, k0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (k0 + kKeyTile >= k_end) break;
+    if (k0 + 2 * kKeyTile < k_end) load(K0, k0 + 2 * kKeyTile);
+    tile(K1, k0 + kKeyTile);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
   l += swap_half(l);
   if (half == 0 && row < p.rows) {
@@ -138,11 +205,12 @@ __global__ __launch_bounds__(kThreads, 4) void score_rowstats(const ScoreParams 
 // ------------------------------------------------------------------ 2. column sums
 template <int D>
 __global__ __launch_bounds__(kThreads, 3) void score_colsum(const ScoreParams p, int rows_pad) {
+  using T = Tile<D>;
   constexpr int NK = D / 16;
-  constexpr int QSTR = D + 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t Q0[T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t Q1[T::ELEMS];
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem);                   // [2][kQChunk][QSTR]
-  float* sL = reinterpret_cast<float*>(smem + 2 * kQChunk * QSTR * 2); // [rows_pad] lse2
+  float* sL = reinterpret_cast<float*>(smem);   // [rows_pad] row lse (log2 units)
 
   const int n_kt = (gridDim.x / (p.v_count * p.hkv));
   int b = blockIdx.x;
@@ -152,6 +220,15 @@ __global__ __launch_bounds__(kThreads, 3) void score_colsum(const ScoreParams p,
   const int lo = p.bs[v], hi = p.bs[v + 1];
   const int kbase = lo + kt * kColKeys;
   if (kbase >= hi) return;
+
+  // packed query-row chunks: chunk c0 is rows c0 .. c0+63 of this KV head's packed rows
+  TileLoader<D> ld;
+  ld.init(D * 2);
+  const uint16_t* qg = p.qp + (int64_t)g * p.q_rows * D;
+  auto load = [&](uint16_t* dst, int c0) {
+    ld.load(dst, qg + (int64_t)c0 * D, (unsigned)(p.q_rows - c0) * (D * 2));
+  };
+  if (p.rows > 0) load(Q0, 0);
 
   // row log-sum-exp (log2 units) from the split statistics, splits in order
   const int nsp = (hi - lo + kScoreSplit - 1) / kScoreSplit;
@@ -185,70 +262,60 @@ __global__ __launch_bounds__(kThreads, 3) void score_colsum(const ScoreParams p,
     for (int ks = 0; ks < NK; ++ks)
       kf[kg][ks] = as_bf16x8(ok ? load16(krow + ks * 16) : u32x4{0, 0, 0, 0});
   }
+  int qofs = l32 * T::STR + half * 8;
+  asm volatile("" : "+v"(qofs));   // keeps each chunk read "array + offset" (see row statistics)
 
-  // query-row chunks: the next chunk is fetched into registers while the current one is
-  // used, then stored into the other LDS stage (one barrier per chunk)
-  constexpr int CPT = kQChunk * D / 8 / kThreads;   // 16-byte chunks per thread per chunk
-  u32x4 pre[CPT];
-  auto fetch = [&](int c0) {
+  float col[2] = {0.f, 0.f};
+  // one 32-row block: S = Q.K^T for the wave's two 32-key groups, probabilities summed
+  // into the column totals (rows past the end have lse = +inf and add 0)
+  auto row_block = [&](const uint16_t* qb, int c0, int rb) {
+    bf16x8 af[NK];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = threadIdx.x + c * kThreads;
-      const int r = c0 + idx / (D / 8), cc = idx % (D / 8);
-      u32x4 val = {0, 0, 0, 0};
-      if (r < p.rows) {
-        const int h = g * p.group + r / p.l_query, qi = r % p.l_query;
-        val = load16(p.qq + ((int64_t)qi * p.hq + h) * D + cc * 8);
-      }
-      pre[c] = val;
+    for (int ks = 0; ks < NK; ++ks)
+      af[ks] = as_bf16x8(load16(qb + qofs + rb * 32 * T::STR + ks * 16));
+    const int rbase = c0 + rb * 32 + 4 * half;
+    float lse[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lse[r] = sL[rbase + 8 * (r / 4) + (r % 4)];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) s = mfma32(af[ks], kf[kg][ks], s);
+      float acc = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc += fast_exp2(fmaf(s[r], p.scale_log2, -lse[r]));
+      col[kg] += acc;
     }
   };
-  fetch(0);
-  __syncthreads();   // the row statistics in sL are complete
-  float col[2] = {0.f, 0.f};
-  int buf = 0;
-  for (int c0 = 0; c0 < p.rows; c0 += kQChunk, buf ^= 1) {
-    uint16_t* sQb = sQ + buf * kQChunk * QSTR;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = threadIdx.x + c * kThreads;
-      store16(sQb + (idx / (D / 8)) * QSTR + (idx % (D / 8)) * 8, pre[c]);
-    }
-    __syncthreads();
-    if (c0 + kQChunk < p.rows) fetch(c0 + kQChunk);
-    // one 32-row block: S = Q.K^T for the wave's two 32-key groups, probabilities summed
-    // into the column totals (rows past the end have lse = +inf and add 0)
-    auto row_block = [&](int rb) {
-      bf16x8 af[NK];
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks)
-        af[ks] = as_bf16x8(load16(sQb + (rb * 32 + l32) * QSTR + ks * 16 + half * 8));
-      const int rbase = c0 + rb * 32 + 4 * half;
-      float lse[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) lse[r] = sL[rbase + 8 * (r / 4) + (r % 4)];
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {
-        f32x16 s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) s = mfma32(af[ks], kf[kg][ks], s);
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc += fast_exp2(fmaf(s[r], p.scale_log2, -lse[r]));
-        col[kg] += acc;
-      }
-    };
+  auto chunk = [&](const uint16_t* qb, int c0) {
     const int nrb = min(kQChunk, p.rows - c0 + 31) / 32;
     if (nrb == kQChunk / 32) {
       // a full chunk as one straight-line block, so the exponentials of one row block
       // overlap the MFMAs of the next
 #pragma unroll
-      for (int rb = 0; rb < kQChunk / 32; ++rb) row_block(rb);
+      for (int rb = 0; rb < kQChunk / 32; ++rb) row_block(qb, c0, rb);
     } else {
-      for (int rb = 0; rb < nrb; ++rb) row_block(rb);
+      for (int rb = 0; rb < nrb; ++rb) row_block(qb, c0, rb);
     }
+  };
+
+  // two LDS stages: chunk i+1 is loaded while chunk i is used, one barrier per chunk (the
+  // first barrier also publishes the row log-sum-exps)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int c0 = 0; c0 < p.rows; c0 += 2 * kQChunk) {
+    if (c0 + kQChunk < p.rows) load(Q1, c0 + kQChunk);
+    chunk(Q0, c0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c0 + kQChunk >= p.rows) break;
+    if (c0 + 2 * kQChunk < p.rows) load(Q0, c0 + 2 * kQChunk);
+    chunk(Q1, c0 + kQChunk);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 #pragma unroll
   for (int kg = 0; kg < 2; ++kg) {
@@ -390,12 +457,15 @@ __global__ __launch_bounds__(kSelThreads) void select_topk(const ScoreParams p) 
 
 }  // namespace
 
-size_t score_workspace_bytes(int n_blocks, int hkv, int rows, int n_split, int n_tokens,
-                             bool need_scores) {
-  size_t stats = (size_t)n_blocks * hkv * n_split * rows * sizeof(float2);
-  stats = (stats + 255) & ~(size_t)255;
-  const size_t sc = need_scores ? (size_t)hkv * n_tokens * sizeof(float) : 0;
-  return stats + sc;
+ScoreWorkspace score_workspace(int n_blocks, int hkv, int rows, int n_split, int n_tokens,
+                               int head_dim, bool need_scores) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  ScoreWorkspace w;
+  w.stats = 0;
+  w.qpack = up((size_t)n_blocks * hkv * n_split * rows * sizeof(float2));
+  w.scores = w.qpack + up((size_t)hkv * score_q_rows(rows) * head_dim * 2);
+  w.total = w.scores + (need_scores ? (size_t)hkv * n_tokens * sizeof(float) : 0);
+  return w;
 }
 
 size_t score_colsum_lds_bytes(int rows, int head_dim) {
@@ -407,6 +477,18 @@ hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block
                                hipStream_t stream) {
   if (p.v_count <= 0) return hipSuccess;
   const int n_rg = (p.rows + 127) / 128;
+  // the packed rows are written by the launch that starts at block 0 (a launch over later
+  // blocks is ordered after it)
+  if (p.rows > 0 && p.v_begin == 0) {
+    const int64_t n = (int64_t)p.hkv * p.q_rows * (head_dim / 8);
+    dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+    if (head_dim == 128)
+      hipLaunchKernelGGL(score_pack_q<128>, grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(score_pack_q<64>, grid, dim3(kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (p.rows > 0) {
     dim3 grid(p.v_count * p.hkv * n_rg * p.n_split);
     if (head_dim == 128)
@@ -419,7 +501,7 @@ hipError_t launch_score_select(const ScoreParams& p, int head_dim, int max_block
   {
     const int n_kt = (max_block + kColKeys - 1) / kColKeys;
     const int rows_pad = ((p.rows + kQChunk - 1) / kQChunk) * kQChunk;
-    const size_t shm = score_colsum_lds_bytes(p.rows, head_dim);
+    const size_t shm = (size_t)(rows_pad > 0 ? rows_pad : 1) * 4;   // the row lse
     dim3 grid(p.v_count * p.hkv * n_kt);
     if (head_dim == 128)
       hipLaunchKernelGGL(score_colsum<128>, grid, dim3(kThreads), shm, stream, p, rows_pad);
