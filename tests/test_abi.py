@@ -412,3 +412,18 @@ def test_layer_forward_validation_before_launch():
     bad = small_layout(head_dim=96)
     io = _lib._LayerIO(*(base[f] for f in _lib._IO_FIELDS), 1 << 20)
     assert L.apbv_layer_forward(bad.ref(), ctypes.byref(io), None) == _lib.APBV_EUNSUPPORTED
+
+
+def test_score_rows_are_limited_by_the_column_sum_lds():
+    """G * l_q score rows share one column-sum workgroup's LDS with two staged query chunks:
+    at head_dim 128 up to 32256 rows (padded to 64) fit in 160 KiB; one more chunk of 64
+    is refused on the host. The accepted layout fails only for its missing workspace."""
+    L = apbv.lib()
+
+    def call(l_query):
+        lay = apbv.Layout([0, 300, 600], l_anchor=32, l_query=l_query, l_pass=32, hq=28,
+                          hkv=4, head_dim=128)
+        return L.apbv_score_select(lay.ref(), 0x1000, 0x2000, None, 0x3000, None, 0, None)
+    assert call(4608) == _lib.APBV_EWORKSPACE      # 7 * 4608 = 32256 rows: fits
+    assert call(4617) == _lib.APBV_EUNSUPPORTED    # 32319 rows, padded to 32320
+    assert "LDS" in L.apbv_last_error().decode()
