@@ -1,8 +1,9 @@
 """Full-size GPU parity against the oracle, through the C ABI, in the launch configuration
 the benchmark times (64K-256K context tokens; needs a GPU). What is compared is described in
 fullsize.py: every block's scores and selection, the gather bitwise, attention teacher-forced
-on whole 256-row tiles (every row at 64K and at both 128K layouts, else a fixed tile sample
-of every block) for one query head per KV group, and the end-to-end prefix identity.
+on whole 256-row tiles (every row of every workload; a fixed tile sample of every block in the
+bucket sweep and for dense causal attention) for one query head per KV group, and the
+end-to-end prefix identity.
 """
 from __future__ import annotations
 
@@ -31,21 +32,12 @@ def _gpu():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["c1", "c2", "c4"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_full_size_every_row(name):
-    """64K, 128K and the variable-frame 128K layout: every row of one query head per KV
-    group."""
+    """64K, 128K, 256K and the variable-frame 128K layout: every row of one query head per
+    KV group."""
     x = generate(workload(name))
     fullsize_check(x, layout_of(x), all_rows=True)
-
-
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["c3"])
-def test_full_size_tile_sample(name):
-    """256K: every block's scores and selection, and attention on a fixed tile sample of
-    every block."""
-    x = generate(workload(name))
-    fullsize_check(x, layout_of(x), all_rows=False)
 
 
 @pytest.mark.timeout(600)
