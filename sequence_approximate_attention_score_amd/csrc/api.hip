@@ -10,7 +10,7 @@
 #include "apbv_internal.h"
 
 // Scratch of the allocation-free scoring entry point (apbv_score_select_noalloc): the split
-// statistics and, when the caller passes no score buffer, the scores. The runtime gives every
+// statistics, the packed score rows and, when the caller passes no score buffer, the scores. The runtime gives every
 // device the library runs on its own copy, held until the process ends. In host code this
 // name is only a stand-in for the symbol: its device address comes from hipGetSymbolAddress
 // (scratch_of_current_device below) and only that address is ever handed to a kernel.
