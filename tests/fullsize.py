@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 import oracle_pool
-from gpu_util import ATOL_MAX, ATOL_MEAN, check_selection, layout_of, say, upload
+from gpu_util import ATOL_MAX, ATOL_MEAN, check_selection, say, upload
 from synthetic import bf16_bits
 import sequence_approximate_attention_score_amd as apbv
 from oracle import apbv_oracle as orc
