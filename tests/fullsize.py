@@ -37,10 +37,15 @@ if torch.cuda.device_count() > 0:     # counting devices does not initialise the
     oracle_pool.start()
 
 
-def one_head_per_group(hq, hkv):
-    """One query head of every KV group, at a different position inside each group."""
+def one_head_per_group(hq, hkv, shift=0):
+    """One query head of every KV group, at a different position inside each group;
+    ``shift`` moves every pick along its group (workloads use different shifts, so that
+    together they cover more heads)."""
     G = hq // hkv
-    return [g * G + (g % G) for g in range(hkv)]
+    return [g * G + (g + shift) % G for g in range(hkv)]
+
+
+HEAD_SHIFT = {"c1": 0, "c2": 1, "c3": 2, "c4": 3}   # 16 distinct heads over the four
 
 
 def compare_attention(out_host, lse_host, bs, results):
@@ -76,7 +81,8 @@ def fullsize_check(x, lay, *, all_rows, heads=None, seed=7, runner=three_calls):
     n = lay.n_blocks
     G = w.hq // w.hkv
     scale = 1.0 / math.sqrt(w.head_dim)
-    heads = one_head_per_group(w.hq, w.hkv) if heads is None else heads
+    if heads is None:
+        heads = one_head_per_group(w.hq, w.hkv, HEAD_SHIFT.get(w.name, 0))
     say(f"case {w.name}: n={n} N={lay.n_tokens} l_a={lay.l_anchor} l_q={w.l_query} "
         f"l_p={lay.l_pass} heads={heads} rows={'all' if all_rows else 'tile sample'}")
     d = upload(x)
