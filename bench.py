@@ -335,9 +335,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the approximate-attention path is built for a single "
+        print("bench.py measures one GPU: the approximate-attention path runs on a single "
               "MI355X (all virtual blocks on one device, no collectives); runs on more than one "
-              "GPU are not part of this build.", file=sys.stderr)
+              "GPU are not supported.", file=sys.stderr)
         sys.exit(2)
 
     from synthetic import generate, sweep_layouts, workload
