@@ -13,7 +13,8 @@
  *      blocks | the block's own keys, causal]                        (apbv_approx_attn_prefill).
  * apbv_prefill_layer runs the three steps in one call, optionally with the selection of later
  * blocks on a second stream beside the attention. The rows of the query block itself, which
- * see the whole sequence, come from apbv_query_forward.
+ * see the whole sequence, come from apbv_query_forward; apbv_layer_forward yields every row
+ * of a layer (anchor, context and query rows) in one call.
  * All virtual blocks of the method's sequence-parallel layout live on one GPU; ZigZag
  * pairing of block p with block n-1-p (same page, "Suddivisione del Contesto e
  * Disposizione ZigZag" and "Bilanciamento del Carico dell'Attenzione Approssimata") is the
