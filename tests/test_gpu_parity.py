@@ -186,6 +186,10 @@ VARIANTS = {
                              l_query=300, l_pass=64), [0, 1200, 2500], {}),
     "d64_several_tiles": (dict(hq=8, hkv=2, head_dim=64, total_tokens=4096, l_anchor=128,
                                l_query=32, l_pass=128), [0, 1024, 2048, 3072, 4096], {}),
+    # no query block: every score is 0 and each block keeps its first l_p rows (ties go to
+    # the lower row)
+    "no_query_block": (dict(hq=4, hkv=2, head_dim=128, total_tokens=600, l_anchor=32,
+                            l_query=0, l_pass=40), [0, 300, 600], {}),
     # G * l_q = 7 * 4600 = 32200 score rows, padded to 32256: the most the column-sum LDS
     # holds at head_dim 128 (one workgroup per CU)
     "max_score_rows": (dict(hq=28, hkv=4, head_dim=128, total_tokens=600, l_anchor=32,
