@@ -253,6 +253,40 @@ def test_fused_qkv_strides():
     assert np.array_equal(host_f64(out), ref["out"])
 
 
+def test_largest_kv_row_stride():
+    """K and V rows 2^22 - 8 elements apart, the largest stride the C ABI accepts (tile loads
+    form 24-bit byte offsets: a row below 64 times a stride below 2^23 bytes). The whole
+    layer equals the layer on contiguous K and V, bit for bit."""
+    x = small("c0", hq=4, hkv=2, head_dim=128, total_tokens=300, n_blocks=2, block_len=150,
+              l_anchor=32, l_query=16, l_pass=24)
+    w = x.w
+    N, d = x.N, w.head_dim
+    stride = (1 << 22) - 8
+    say(f"  K/V row stride {stride} elements: {2 * N * stride * 2 / 2**30:.1f} GiB of buffers")
+    views = {}
+    for n in ("k_ctx", "v_ctx"):
+        big = torch.zeros(N * stride, dtype=torch.bfloat16, device="cuda")
+        rows = big.view(N, stride)
+        rows[:, : w.hkv * d] = dev_bf16(x.bits[n].reshape(N, -1))
+        views[n] = rows[:, : w.hkv * d]
+    lay = layout_of(x, kv_row_stride=stride)
+    dd = upload(x, ("q_query", "q_ctx", "k_anchor", "v_anchor"))
+    scores, sel = apbv.score_select(lay, dd["q_query"], views["k_ctx"])
+    kp, vp = apbv.gather_passing(lay, dd["k_anchor"], dd["v_anchor"], views["k_ctx"],
+                                 views["v_ctx"], sel)
+    out, lse = apbv.approx_attn_prefill(lay, dd["q_ctx"], kp, vp, views["k_ctx"],
+                                        views["v_ctx"], want_lse=True)
+    torch.cuda.synchronize()
+    ref = run_gpu(x, layout_of(x), upload(x))
+    assert np.array_equal(scores.cpu().numpy(), ref["scores"])
+    assert np.array_equal(sel.cpu().numpy(), ref["sel"])
+    assert np.array_equal(host_f64(kp), ref["k_pre"]) and np.array_equal(host_f64(vp), ref["v_pre"])
+    assert np.array_equal(host_f64(out), ref["out"])
+    assert np.array_equal(lse.cpu().numpy().astype(np.float64), ref["lse"])
+    del views
+    torch.cuda.empty_cache()
+
+
 def test_zigzag_ranges_and_determinism():
     """Same bits with and without ZigZag, run twice, and bucket by bucket."""
     x = small("c0", hq=4, hkv=2, head_dim=128, total_tokens=6 * 300, n_blocks=6, block_len=300,
