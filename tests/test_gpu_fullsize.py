@@ -41,6 +41,14 @@ def test_full_size_every_row(name):
 
 
 @pytest.mark.timeout(600)
+def test_full_size_every_head_128k():
+    """128K: every one of the 28 query heads on the fixed tile sample of every block (the
+    every-row checks above take one head per KV group)."""
+    x = generate(workload("c2"))
+    fullsize_check(x, layout_of(x), all_rows=False, heads=list(range(x.w.hq)), seed=13)
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["buckets_2", "buckets_4", "buckets_6", "no_passing"])
 def test_sweep_128k(name):
     """The bucket-count sweep (2, 4, 6 buckets over 128K tokens; 8 is the headline layout)
